@@ -1,0 +1,23 @@
+"""CPU oracle for exact tiled attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 numpy implementations of what the GPU library computes.  It
+shares no code with the HIP path and the HIP path never imports it: only the
+tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import or run anything in this package.
+
+Sources (page titles of the reference text):
+  [IO]   "M4.3 - IO-Aware Attention and FlashAttention-1: Online Softmax, Tiling,
+          and Exactness"
+  [FA2]  "M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary"
+  [HW]   "M4.6 - FlashAttention-3/4 Hardware Pipelines: Hopper, Blackwell, and
+          the Moving Bottleneck"
+
+Modules:
+  dense   -- the dense definition (forward, LSE, backward, decode)   [pinned]
+  state   -- the online (m, l, u, n) state algebra and its merges     [pinned]
+  fp8     -- the E4M3FN codebook and the quantised forward steps      [codebook,
+             the 2^8 cancellation and the no-rounding reduction are pinned;
+             parity of the quantised output itself is unpinned: no printed values
+             exist for this input distribution]
+  tiles   -- causal tile classes and visit counts                    [pinned]
+"""

@@ -1,0 +1,137 @@
+"""E4M3FN arithmetic and the quantised attention forward.  Test infrastructure only.
+
+Codebook ([HW] section 0x06, "E4M3 Names The Operand"): one sign bit, four exponent
+bits (bias 7), three fraction bits; finite-only, largest magnitude 448, smallest
+positive subnormal 2^-9; the all-ones exponent with all-ones fraction is NaN.
+
+Quantised forward ([HW] 0x06, "Derive Where Every Scale Must Enter" and "Why The
+Source Raises Softmax Probabilities By 2^8"), per batch item, query head and K/V
+tile j taken in ascending key order:
+
+    S     = scale * dQ_i * dK_j * (Q8 K8_j^T)          (descales before the row max)
+    m_new = max(m, rowmax S),  alpha = exp(m - m_new)
+    u     = 2^8 exp(S - m_new)                         (float, unrounded)
+    p8    = E4M3(u)                                    (round to nearest even, saturating)
+    l     = alpha l + rowsum(u)                        (denominator from unrounded u)
+    o     = alpha o + dV_j * (p8 V8_j)                 (per-tile V descale)
+    O     = o / l,   LSE = m + ln l - 8 ln 2.
+
+Parity of this quantised output is unpinned by printed values: the pages print no
+result for this input distribution.  What is pinned: the codebook against an
+independent float8 implementation, the exact 2^8 cancellation, and that with the
+probability rounding removed the steps reproduce the dense definition.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+E4M3_MAX = 448.0
+PROB_OFFSET_LOG2 = 8
+
+
+def decode_code(c: int) -> float:
+    """Value of one E4M3FN byte from its bit fields."""
+    c = int(c) & 0xFF
+    sign = -1.0 if c & 0x80 else 1.0
+    e = (c >> 3) & 0xF
+    f = c & 0x7
+    if e == 0xF and f == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (f / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + f / 8.0) * 2.0 ** (e - 7)
+
+
+_TABLE = np.array([decode_code(c) for c in range(256)], dtype=np.float64)
+# non-negative finite codes 0x00..0x7E are increasing in value
+_POS_VALUES = _TABLE[:0x7F]
+
+
+def decode(codes) -> np.ndarray:
+    """Array of E4M3FN bytes (uint8, any shape) -> float64 values."""
+    c = np.asarray(codes.cpu().numpy() if hasattr(codes, "cpu") else codes).astype(np.uint8)
+    return _TABLE[c]
+
+
+def encode_rne_sat(x) -> np.ndarray:
+    """float64 -> E4M3FN codes: round to nearest, ties to even code, saturate at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_POS_VALUES, a, side="left")          # first value >= a
+    hi = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _POS_VALUES[lo]
+    dhi = _POS_VALUES[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == _POS_VALUES[hi], hi, code).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def round_e4m3(x) -> np.ndarray:
+    return _TABLE[encode_rne_sat(x)]
+
+
+def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 64,
+            scale_rows: int = 128, rows=None, heads=None, prob_round=round_e4m3, frame="running"):
+    """The quantised forward, step by step (non-causal).
+
+    q8/k8/v8: E4M3FN codes [B,H,S,d] (uint8); *_scale: float32 [B,H,ceil(S/128)].
+    ``block_c``: K/V tile width; each tile must lie inside one 128-row scale block.
+    ``prob_round``: the probability rounding (identity removes it).
+    ``frame``: "running" rounds u in the running-max frame (the kernel's order);
+    "final" rounds it in the final row-max frame (an informational variant).
+    Returns (O [B,Hq,R,d], LSE [B,Hq,R]) in float64.
+    """
+    assert scale_rows % block_c == 0, "a K/V tile must lie inside one scale block"
+    Q, K, V = decode(q8), decode(k8), decode(v8)
+    qs, ks, vs = (np.asarray(t.cpu().numpy() if hasattr(t, "cpu") else t, dtype=np.float64)
+                  for t in (q_scale, k_scale, v_scale))
+    B, Hq, Sq, _ = Q.shape
+    Hkv, Sk = K.shape[1], K.shape[2]
+    g = Hq // Hkv
+    rows = np.arange(Sq) if rows is None else np.asarray(rows)
+    O = np.full((B, Hq, len(rows), V.shape[3]), np.nan)
+    LSE = np.full((B, Hq, len(rows)), np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
+    off = float(2 ** PROB_OFFSET_LOG2)
+    for b, h in pairs:
+        kv = h // g
+        Qi = Q[b, h][rows]
+        dq = qs[b, h][rows // scale_rows]
+        if frame == "final":
+            S_all = float(scale) * dq[:, None] * (Qi @ K[b, kv].T) * ks[b, kv][np.arange(Sk) // scale_rows][None, :]
+            m_final = S_all.max(axis=1)
+        m = np.full(len(rows), -np.inf)
+        l = np.zeros(len(rows))
+        o = np.zeros((len(rows), V.shape[3]))
+        for k0 in range(0, Sk, block_c):
+            k1 = min(Sk, k0 + block_c)
+            dk = ks[b, kv][k0 // scale_rows]
+            dv = vs[b, kv][k0 // scale_rows]
+            S = float(scale) * dq[:, None] * dk * (Qi @ K[b, kv][k0:k1].T)
+            m_new = np.maximum(m, S.max(axis=1))
+            alpha = np.exp(m - m_new)
+            u = off * np.exp(S - m_new[:, None])
+            if frame == "final":
+                # the same u expressed in the final frame, rounded there, brought back
+                shift = np.exp(m_new - m_final)[:, None]
+                p8 = prob_round(u * shift) / shift
+            else:
+                p8 = prob_round(u)
+            l = alpha * l + u.sum(axis=1)
+            o = alpha[:, None] * o + dv * (p8 @ V[b, kv][k0:k1])
+            m = m_new
+        O[b, h] = o / l[:, None]
+        LSE[b, h] = m + np.log(l) - PROB_OFFSET_LOG2 * math.log(2.0)
+    return O, LSE
+
+
+def dequantized(codes, scales, scale_rows: int = 128) -> np.ndarray:
+    """float64 values decode(code) * descale of each row's block: [B,H,S,d]."""
+    X = decode(codes)
+    s = np.asarray(scales.cpu().numpy() if hasattr(scales, "cpu") else scales, dtype=np.float64)
+    S = X.shape[2]
+    return X * s[:, :, np.arange(S) // scale_rows][..., None]

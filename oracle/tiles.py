@@ -1,0 +1,42 @@
+"""Causal tile geometry from integer coordinates.  Test infrastructure only.
+
+[FA2] section 0x05.1A-B: query tile i covers [q0, q1) = [i B_r, min(S_q,(i+1)B_r)),
+key tile j covers [k0, k1) = [j B_c, min(S_k,(j+1)B_c)); a cell is visible iff
+k <= q + delta.  A tile is skipped (fully future) iff k0 > (q1 - 1) + delta, fully
+visible iff (k1 - 1) <= q0 + delta, and partial otherwise.
+"""
+from __future__ import annotations
+
+
+def tile_class(q0, q1, k0, k1, delta):
+    if k0 > (q1 - 1) + delta:
+        return "skipped"
+    if (k1 - 1) <= q0 + delta:
+        return "full"
+    return "partial"
+
+
+def ranges(n, block):
+    return [(s, min(n, s + block)) for s in range(0, n, block)]
+
+
+def census(sq, sk, br, bc, delta):
+    """Counts of tile classes and cells over the whole [S_q, S_k] grid."""
+    out = {"full": 0, "partial": 0, "skipped": 0, "visited_cells": 0, "allowed_cells": 0}
+    for q0, q1 in ranges(sq, br):
+        for k0, k1 in ranges(sk, bc):
+            c = tile_class(q0, q1, k0, k1, delta)
+            out[c] += 1
+            if c != "skipped":
+                out["visited_cells"] += (q1 - q0) * (k1 - k0)
+                for q in range(q0, q1):
+                    hi = min(k1, q + delta + 1)
+                    out["allowed_cells"] += max(0, hi - k0)
+    out["visited"] = out["full"] + out["partial"]
+    return out
+
+
+def visited_per_query_tile(sq, sk, br, bc, delta):
+    """Number of non-skipped key tiles for each query tile."""
+    return [sum(1 for k0, k1 in ranges(sk, bc) if tile_class(q0, q1, k0, k1, delta) != "skipped")
+            for q0, q1 in ranges(sq, br)]
