@@ -1,0 +1,121 @@
+"""exact_tiled_attention_amd -- Python binding of libattn (gfx950 HIP kernels).
+
+Argument marshalling only: every step of attention runs in the library's kernels.
+torch supplies device memory and the current stream.  Importing this package does
+not touch the GPU; the first call loads libattn.so and raises if it is missing.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import AttnError, LibraryMissing, lib
+
+__all__ = ["attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+           "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
+           "AttnError", "LibraryMissing", "lib"]
+
+_CODES = {torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16, torch.float32: _lib.ATTN_F32}
+
+
+def _code(dtype):
+    if dtype not in _CODES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _CODES[dtype]
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _require(t, name, ndim):
+    if t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {ndim}-d CUDA tensor")
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
+    """O, LSE = attention(q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d]); fp16/bf16; LSE float32."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, 4)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                        scale, int(bool(causal)), _code(q.dtype), _stream(stream))
+    _lib.check("attn_fwd", st)
+    return o, lse
+
+
+def fp8_kv_tile() -> int:
+    return lib().attn_fp8_kv_tile()
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale=None, o_dtype=torch.bfloat16,
+                 o=None, lse=None, stream=None):
+    """Forward on E4M3FN codes (uint8 or float8_e4m3fn tensors) with 128-row-block descales."""
+    B, Hq, Sq, d = q8.shape
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, Hq, Sq, d), dtype=o_dtype, device=q8.device) if o is None else o
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device) if lse is None else lse
+    st = lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, scale, 0, _code(o.dtype),
+                            _stream(stream))
+    _lib.check("attn_fwd_fp8", st)
+    return o, lse
+
+
+def bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d) -> int:
+    return lib().attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
+
+
+def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.float32,
+             workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """dQ, dK, dV of attn_fwd (dK/dV already summed over each K/V head's query group)."""
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device) if dv is None else dv
+    need = bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                        _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), _code(q.dtype),
+                        _code(grad_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(stream))
+    _lib.check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def decode_workspace_size(B, Hq, Smax, d, chunk=256) -> int:
+    return lib().attn_decode_workspace_size(B, Hq, Smax, d, chunk)
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=256, workspace=None,
+                        o=None, lse=None, stream=None):
+    """Split-KV decode: q [B,Hq,1,d], caches [B,Hkv,Smax,d], seqlens int32 [B] on device."""
+    B, Hq, _, d = q.shape
+    Hkv, Smax = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_size(B, Hq, Smax, d, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().attn_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
+                                   B, Hq, Hkv, Smax, d, scale, chunk, _code(q.dtype), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("attn_decode_splitkv", st)
+    return o, lse

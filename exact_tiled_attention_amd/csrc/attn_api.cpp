@@ -1,0 +1,180 @@
+// attn_api.cpp -- the C ABI of libattn: argument checks (pure host, before any HIP
+// call), workspace sizing and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+#include "tile_plan.h"
+
+namespace {
+
+constexpr int kMaxSeq = 1 << 20;
+constexpr int kMaxBH = 1 << 16;
+
+int check_dims(int B, int Hq, int Hkv, int Sq, int Sk, int d, bool allow_sk0) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0) return ATTN_ERR_SHAPE;
+  if (Sk < 0 || (!allow_sk0 && Sk == 0)) return ATTN_ERR_SHAPE;
+  if (Sq > kMaxSeq || Sk > kMaxSeq) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * Hq > kMaxBH) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int decode_chunks(int Smax, int chunk) { return (Smax + chunk - 1) / chunk; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid or too large tensor size";
+    case ATTN_ERR_GQA: return "H_q is not a multiple of H_kv";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension";
+    case ATTN_ERR_DTYPE: return "unsupported element type";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch or runtime error";
+    case ATTN_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int attn_tile_plan(int q_begin, int q_end, int Sq, int Sk, int block_k, int causal,
+                   int* n_visit, int* first_masked) {
+  if (n_visit == nullptr || first_masked == nullptr) return ATTN_ERR_NULL;
+  if (block_k <= 0 || Sq <= 0 || Sk < 0 || q_begin < 0 || q_end <= q_begin || q_end > Sq)
+    return ATTN_ERR_ARG;
+  const TilePlan p = plan_rows(q_begin, q_end, Sq, Sk, block_k, causal != 0);
+  *n_visit = p.n_visit;
+  *first_masked = p.first_masked;
+  return ATTN_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             attn_dtype_t dtype, void* stream) {
+  if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (Sk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, true);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  FwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
+}
+
+int attn_fp8_kv_tile(void) { return attn_fp8_tile_keys(); }
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                 const float* q_scale, const float* k_scale, const float* v_scale,
+                 void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                 float scale, int causal, attn_dtype_t o_dtype, void* stream) {
+  if (q8 == nullptr || k8 == nullptr || v8 == nullptr || q_scale == nullptr ||
+      k_scale == nullptr || v_scale == nullptr || o == nullptr)
+    return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, false);
+  if (st != ATTN_OK) return st;
+  if (d != 128) return ATTN_ERR_HEADDIM;
+  if (causal) return ATTN_ERR_ARG;
+  if (o_dtype != ATTN_BF16 && o_dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  Fp8Args a = {};
+  a.q = (const uint8_t*)q8; a.k = (const uint8_t*)k8; a.v = (const uint8_t*)v8;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.o_f32 = o_dtype == ATTN_F32;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(attn_launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
+  if (check_dims(B, Hq, Hkv, Sq, Sk, d, false) != ATTN_OK) return 0;
+  const size_t rows = (size_t)B * Hq * Sq;
+  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             attn_dtype_t dtype, attn_dtype_t grad_dtype,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+      dO == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, false);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (grad_dtype != ATTN_F32 && grad_dtype != ATTN_BF16 && grad_dtype != ATTN_F16)
+    return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * Hq * Sq;
+  BwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dO = dO;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = (float*)workspace;
+  a.delta = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.grad_type = (int)grad_dtype;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int Smax, int d, int chunk) {
+  if (B <= 0 || Hq <= 0 || Smax <= 0 || Smax > kMaxSeq || (int64_t)B * Hq > kMaxBH) return 0;
+  if ((d != 64 && d != 128) || chunk <= 0 || chunk % 64 != 0) return 0;
+  const size_t parts = (size_t)B * Hq * decode_chunks(Smax, chunk);
+  return align256(parts * 2 * sizeof(float)) + align256(parts * d * sizeof(float));
+}
+
+int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                        const int* seqlens_k, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
+                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || seqlens_k == nullptr ||
+      o == nullptr)
+    return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, 1, Smax, d, false);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (chunk <= 0 || chunk % 64 != 0 || chunk > 4096 || !isfinite(scale)) return ATTN_ERR_ARG;
+  const size_t need = attn_decode_workspace_size(B, Hq, Smax, d, chunk);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  DecodeArgs a = {};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.seqlens = seqlens_k; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Smax = Smax; a.d = d; a.chunk = chunk;
+  a.nchunk = decode_chunks(Smax, chunk);
+  const size_t parts = (size_t)B * Hq * a.nchunk;
+  a.part_ml = (float*)workspace;
+  a.part_u = (float*)((char*)workspace + align256(parts * 2 * sizeof(float)));
+  a.group = Hq / Hkv;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(attn_launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// attn_device.h -- gfx950 device helpers: element types, MFMA wrappers, lane layouts.
+//
+// Matrix-core layout used throughout (v_mfma_f32_32x32x16_{f16,bf16}, wave64):
+//   A operand (32 x 16, M x K): lane l holds row  m = l % 32 and 8 contraction slots
+//   B operand (16 x 32, K x N): lane l holds column n = l % 32 and the same 8 slots
+//   C/D       (32 x 32)       : lane l holds column n = l % 32, register i holds row
+//                               m = 8 * (i / 4) + 4 * (l / 32) + (i % 4).
+// The contraction slots of lane l are the 8 values of lane group g = l / 32; A and B
+// pair slot-for-slot, so any consistent assignment of contraction indices to
+// (g, slot) is a valid product.  The kernels choose that assignment per product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+#define ATTN_LOG2E 1.4426950408889634f
+#define ATTN_LN2 0.6931471805599453f
+
+// Element traits: 8-wide operand vector and conversions.
+template <typename T> struct Elem;
+template <> struct Elem<f16> {
+  typedef f16x8 v8;
+  static __device__ inline float to_f(f16 x) { return (float)x; }
+  static __device__ inline f16 from_f(float x) { return (f16)x; }
+  static __device__ inline uint32_t pack2(float a, float b) {
+    f16x2 h;
+    h.x = (f16)a;
+    h.y = (f16)b;
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  static __device__ inline f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Elem<bf16> {
+  typedef bf16x8 v8;
+  static __device__ inline float to_f(bf16 x) { return (float)x; }
+  static __device__ inline bf16 from_f(float x) { return (bf16)x; }
+  static __device__ inline uint32_t pack2(float a, float b) {
+    bf16x2 h;
+    h.x = (bf16)a;
+    h.y = (bf16)b;
+    return __builtin_bit_cast(uint32_t, h);
+  }
+  static __device__ inline f32x16 mfma(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename V> __device__ inline V as_v8(const u32x4& u) { return __builtin_bit_cast(V, u); }
+
+__device__ inline u32x4 ld_global_16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st_global_16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ inline u32x4 ld_lds_16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline u32x2 ld_lds_8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ inline void st_lds_16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ inline void st_lds_8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ inline float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ inline float wave_sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-bit lane interleave helpers for the register transpose of 4 rows x 8 columns.
+// lo16(a) | lo16(b) << 16  and  hi16(a) | hi16(b) << 16.
+__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }

@@ -1,0 +1,300 @@
+// attn_fwd.hip -- tiled attention forward for gfx950 (fp16 / bf16, d = 64 / 128).
+//
+// Schedule ("M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary",
+// section 0x03, Algorithm 1, and section 0x05C, split-Q): one workgroup owns one
+// query tile of one (batch, query head); each of its NW waves owns 32 disjoint query
+// rows, so no output is ever merged across waves.  The workgroup streams K/V tiles of
+// BC keys through a double-buffered LDS ring and every wave carries the online state
+// (m, l, u) of its rows in registers ("M4.3 - IO-Aware Attention ...", section 0x09C;
+// FA2 section 0x02C: u <- alpha u + P~ V, normalised once at the end).
+//
+// Orientation.  The kernel computes the transposed score tile S^T = K Q^T on the
+// 32x32x16 matrix core: in the accumulator layout each lane then holds ONE query
+// column and 16 keys of it, so the running max, the rescale factor alpha and l are
+// per-lane scalars (one cross-lane exchange, lane l <-> l^32, for the max).  The
+// probabilities stay in registers and feed O^T += V^T P^T directly as the B operand:
+// slot j of lane group g in key chunk c is key 16c + 8(j/4) + 4g + j%4, the same
+// keys the S^T accumulator put in registers 8(c%2) .. 8(c%2)+7.  V^T therefore sits
+// in LDS transposed ([d][key]); the transpose happens on the way in, in registers.
+//
+// Exponentials run in base 2 with scale * log2(e) folded into the score scale.
+// Masking (key tail and causal band) is applied before the row max, and only on the
+// tiles the tile plan marks (tile_plan.h).
+#include "attn_device.h"
+#include "attn_launch.h"
+#include "tile_plan.h"
+
+namespace {
+
+constexpr int kWave = 64;
+
+template <int D, int BC>
+struct FwdLds {
+  static constexpr int KSTR = D + 8;     // K row stride (elements): 16-byte pad
+  static constexpr int VSTR = BC + 4;    // V^T row stride (elements): 8-byte pad
+  static constexpr int K_ELEMS = BC * KSTR;
+  static constexpr int V_ELEMS = D * VSTR;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int BYTES = 2 * STAGE * 2;   // two stages of 16-bit elements
+};
+
+template <typename T, int D, int BC, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * kWave) void fwd_kernel(FwdArgs a) {
+  typedef Elem<T> E;
+  typedef typename E::v8 V8;
+  typedef FwdLds<D, BC> L;
+  constexpr int NT = NW * kWave;
+  constexpr int BQ = NW * 32;
+  constexpr int KC = D / 16;                  // contraction chunks for S^T
+  constexpr int KB = BC / 32;                 // key blocks of 32 per tile
+  constexpr int DB = D / 32;                  // output d blocks of 32
+  constexpr int PC = BC / 16;                 // key chunks of 16 for P V
+  constexpr int K_LOADS = (BC * D / 8 + NT - 1) / NT;   // 16-byte K loads per thread
+  constexpr int V_BLOCKS = (BC / 4) * (D / 8);          // 4-key x 8-d transpose blocks
+  constexpr int V_LOADS = (V_BLOCKS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) T lds[2 * L::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int grp = lane >> 5;
+
+  const int BH = a.B * a.Hq;
+  const int wg = blockIdx.x;
+  const int bh = wg % BH;
+  const int qt = CAUSAL ? (a.nqt - 1 - wg / BH) : (wg / BH);   // heavy causal tiles first
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int kvh = h / a.group;
+
+  const T* __restrict__ qb = reinterpret_cast<const T*>(a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
+  const T* __restrict__ kb = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const T* __restrict__ vb = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+
+  const int q0 = qt * BQ;
+  const int q1 = min(q0 + BQ, a.Sq);
+  const int qrow = q0 + w * 32 + n;
+  const TilePlan plan = plan_rows(q0, q1, a.Sq, a.Sk, BC, CAUSAL);
+  const int w0 = q0 + w * 32;
+  const int w1 = max(min(w0 + 32, a.Sq), w0 + 1);
+  const TilePlan wplan = plan_rows(w0, w1, a.Sq, a.Sk, BC, CAUSAL);
+  const int delta = a.Sk - a.Sq;
+
+  // Q^T fragments (B operand): lane column = its query row, slots = d 16kc+8g .. +8.
+  V8 qf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qrow < a.Sq) raw = ld_global_16(qb + (int64_t)qrow * D + 16 * kc + 8 * grp);
+    qf[kc] = as_v8<V8>(raw);
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
+  float m_i = -INFINITY;   // running max (base-2 units)
+  float l_i = 0.f;         // this lane's share of the running denominator
+
+  u32x4 kreg[K_LOADS];
+  u32x4 vreg[V_LOADS][4];
+
+  auto load_tile = [&](int t) {
+    const int k0 = t * BC;
+#pragma unroll
+    for (int r = 0; r < K_LOADS; ++r) {
+      const int idx = r * NT + tid;
+      const int row = idx / (D / 8);
+      const int c8 = idx % (D / 8);
+      const int key = k0 + row;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (idx < BC * D / 8 && key < a.Sk) val = ld_global_16(kb + (int64_t)key * D + c8 * 8);
+      kreg[r] = val;
+    }
+#pragma unroll
+    for (int r = 0; r < V_LOADS; ++r) {
+      const int blk = r * NT + tid;
+      const int kq = blk / (D / 8);
+      const int dc = blk % (D / 8);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int key = k0 + 4 * kq + s;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (blk < V_BLOCKS && key < a.Sk) val = ld_global_16(vb + (int64_t)key * D + dc * 8);
+        vreg[r][s] = val;
+      }
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    T* ks = lds + stage * L::STAGE;
+    T* vs = ks + L::K_ELEMS;
+#pragma unroll
+    for (int r = 0; r < K_LOADS; ++r) {
+      const int idx = r * NT + tid;
+      if (idx < BC * D / 8) {
+        const int row = idx / (D / 8);
+        const int c8 = idx % (D / 8);
+        st_lds_16(ks + row * L::KSTR + c8 * 8, kreg[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < V_LOADS; ++r) {
+      const int blk = r * NT + tid;
+      if (blk < V_BLOCKS) {
+        const int kq = blk / (D / 8);
+        const int dc = blk % (D / 8);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          // dword wd of each of the 4 rows holds d columns 2wd and 2wd+1
+          u32x2 even, odd;
+          even.x = pack_lo(vreg[r][0][wd], vreg[r][1][wd]);
+          even.y = pack_lo(vreg[r][2][wd], vreg[r][3][wd]);
+          odd.x = pack_hi(vreg[r][0][wd], vreg[r][1][wd]);
+          odd.y = pack_hi(vreg[r][2][wd], vreg[r][3][wd]);
+          st_lds_8(vs + (dc * 8 + 2 * wd) * L::VSTR + 4 * kq, even);
+          st_lds_8(vs + (dc * 8 + 2 * wd + 1) * L::VSTR + 4 * kq, odd);
+        }
+      }
+    }
+  };
+
+  auto compute_tile = [&](int t, int stage) {
+    const T* ks = lds + stage * L::STAGE;
+    const T* vs = ks + L::K_ELEMS;
+    f32x16 s[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) s[i] = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+      for (int kbk = 0; kbk < KB; ++kbk) {
+        const V8 av = as_v8<V8>(ld_lds_16(ks + (kbk * 32 + n) * L::KSTR + 16 * kc + 8 * grp));
+        s[kbk] = E::mfma(av, qf[kc], s[kbk]);
+      }
+    }
+    const bool masked = t >= wplan.first_masked;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = s[kbk][i] * a.scale_log2;
+        if (masked) {
+          const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
+          const bool vis = key < a.Sk && (!CAUSAL || key <= qrow + delta);
+          x = vis ? x : -INFINITY;
+        }
+        s[kbk][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = wave_max_xor32(mx);
+    const float m_new = fmaxf(m_i, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_i - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(s[kbk][i] - m_use);
+        s[kbk][i] = pv;
+        rs += pv;
+      }
+    }
+    l_i = alpha * l_i + rs;
+    m_i = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      const int kbk = c >> 1;
+      const int hb = (c & 1) * 8;
+      u32x4 pk;
+      pk.x = E::pack2(s[kbk][hb + 0], s[kbk][hb + 1]);
+      pk.y = E::pack2(s[kbk][hb + 2], s[kbk][hb + 3]);
+      pk.z = E::pack2(s[kbk][hb + 4], s[kbk][hb + 5]);
+      pk.w = E::pack2(s[kbk][hb + 6], s[kbk][hb + 7]);
+      const V8 pb = as_v8<V8>(pk);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const T* vrow = vs + (db * 32 + n) * L::VSTR + 16 * c + 4 * grp;
+        const u32x2 lo = ld_lds_8(vrow);
+        const u32x2 hi = ld_lds_8(vrow + 8);
+        u32x4 av4;
+        av4.x = lo.x;
+        av4.y = lo.y;
+        av4.z = hi.x;
+        av4.w = hi.y;
+        o[db] = E::mfma(as_v8<V8>(av4), pb, o[db]);
+      }
+    }
+  };
+
+  const int nt = plan.n_visit;
+  if (nt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < nt) load_tile(t + 1);
+    if (t < wplan.n_visit) compute_tile(t, stage);
+    if (t + 1 < nt) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: O = u / l once per row; LSE = (m + log2 l) ln 2 (FA2 section 0x02D).
+  const float l_tot = l_i + __shfl_xor(l_i, 32);
+  const bool empty = (m_i == -INFINITY) || !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  if (qrow < a.Sq) {
+    T* ob = reinterpret_cast<T*>(a.o) + ((int64_t)(b * a.Hq + h) * a.Sq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 pk;
+        pk.x = E::pack2(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
+        pk.y = E::pack2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(ob + db * 32 + 8 * r4 + 4 * grp) = pk;
+      }
+    }
+    if (a.lse != nullptr && grp == 0) {
+      a.lse[(int64_t)(b * a.Hq + h) * a.Sq + qrow] = empty ? -INFINITY : (m_i + __log2f(l_tot)) * ATTN_LN2;
+    }
+  }
+}
+
+template <typename T, int D, int BC, int NW>
+hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
+  FwdArgs a = a0;
+  constexpr int BQ = NW * 32;
+  a.nqt = (a.Sq + BQ - 1) / BQ;
+  const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
+  const dim3 block(NW * kWave);
+  if (a.causal)
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fwd_dtype(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 64) return launch_fwd_t<T, 64, 64, 4>(a, stream);
+  return launch_fwd_t<T, 128, 64, 4>(a, stream);
+}
+
+}  // namespace
+
+hipError_t attn_launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  if (a.dtype_bf16) return launch_fwd_dtype<bf16>(a, stream);
+  return launch_fwd_dtype<f16>(a, stream);
+}

@@ -1,0 +1,79 @@
+// attn_launch.h -- internal launcher interface between the C ABI layer and the kernels.
+// Argument checking happens in attn_api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk, d;
+  int group;          // Hq / Hkv
+  int causal;
+  int dtype_bf16;     // 1: bf16, 0: fp16
+  float scale_log2;   // scale * log2(e)
+  int nqt;            // query tiles (filled by the launcher)
+};
+
+struct Fp8Args {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk, d;
+  int group;
+  int o_f32;          // 1: float32 output, 0: bf16 output
+  float scale_log2;
+  int nqt;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;      // [B,Hq,Sq,d] float32 workspace
+  float* delta;       // [B,Hq,Sq]  float32 workspace (D rows, pre-scaled)
+  int B, Hq, Hkv, Sq, Sk, d;
+  int group;
+  int causal;
+  int dtype_bf16;
+  int grad_type;      // attn_dtype_t of dq/dk/dv
+  float scale;
+  float scale_log2;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* seqlens;
+  void* o;
+  float* lse;
+  float* part_ml;     // [B*Hq, nchunk, 2] float32 (m in base 2, l)
+  float* part_u;      // [B*Hq, nchunk, d] float32
+  int B, Hq, Hkv, Smax, d, chunk, nchunk;
+  int group;
+  int dtype_bf16;
+  float scale_log2;
+};
+
+hipError_t attn_launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
+int attn_fp8_tile_keys();
+hipError_t attn_launch_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t attn_launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -1,0 +1,171 @@
+/*
+ * attn.h -- C ABI of libattn, exact tiled attention for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (all entry points): exact dense attention
+ *     O = softmax(scale * Q K^T + mask) V,   LSE = log-sum-exp of each masked score row
+ * computed tile by tile without materialising the [S_q, S_k] score or probability
+ * matrices ("M4.3 - IO-Aware Attention and FlashAttention-1", sections 0x08-0x09;
+ * "M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary", sections
+ * 0x02-0x03).
+ *
+ * Conventions shared by every call
+ *   - Tensors are contiguous row-major [B, H, S, d] ("BHSD") in device memory owned
+ *     by the caller.  The library never allocates or frees device memory: scratch is
+ *     passed in as a workspace whose size the matching *_workspace_size() returns.
+ *   - Query head h reads K/V head h / (H_q / H_kv); H_q must be a multiple of H_kv
+ *     (M4.4, section 0x06A).  Output and LSE are indexed by query head.
+ *   - causal != 0 makes cell (i, k) visible iff k <= i + (S_k - S_q), the bottom-right
+ *     alignment (M4.4, section 0x05.1F).  A query row with no visible key (only
+ *     possible when S_q > S_k) gets O = 0 and LSE = -inf and adds no gradient.
+ *   - LSE is natural-log, float32, [B, H_q, S_q].
+ *   - Supported head dimension d: 64 and 128.  Supported element types: ATTN_F16 and
+ *     ATTN_BF16 (ATTN_FP8_E4M3 only through attn_fwd_fp8).
+ *   - Every call checks its arguments on the host before any HIP call and returns a
+ *     negative status without touching the GPU when they are invalid.  Valid calls
+ *     are asynchronous on `stream` (a hipStream_t; NULL = the default stream); the
+ *     results are ready after the stream is synchronised.  A failed launch returns
+ *     ATTN_ERR_HIP.  The library keeps no state between calls.
+ *   - Sizes are int (each dimension and each product used for indexing must fit the
+ *     64-bit offsets the kernels use; S_q, S_k <= 2^20, B*H <= 2^16 are enforced).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F16 = 0,
+  ATTN_BF16 = 1,
+  ATTN_F32 = 2,
+  ATTN_FP8_E4M3 = 3
+} attn_dtype_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,      /* a required pointer is NULL                              */
+  ATTN_ERR_SHAPE = -2,     /* a size is <= 0 (or S_k < 0), or exceeds the limits above */
+  ATTN_ERR_GQA = -3,       /* H_q is not a multiple of H_kv                            */
+  ATTN_ERR_HEADDIM = -4,   /* d is not 64 or 128                                       */
+  ATTN_ERR_DTYPE = -5,     /* unsupported element / output / gradient type            */
+  ATTN_ERR_WORKSPACE = -6, /* workspace missing or smaller than *_workspace_size()     */
+  ATTN_ERR_HIP = -7,       /* a HIP launch or runtime call failed                      */
+  ATTN_ERR_ARG = -8        /* another argument is out of its range (chunk, scale)      */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * attn_fwd -- tiled forward with saved log-sum-exp.
+ * "M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary", section 0x03
+ * (Algorithm 1: one owner per query tile streams K/V tiles, carries (m, l, u) on chip,
+ * normalises once and commits O and LSE once) and section 0x02D (O = u / l,
+ * LSE = m + log l).
+ *
+ *   q   [B, Hq,  Sq, d]  element type `dtype`          (in)
+ *   k,v [B, Hkv, Sk, d]  element type `dtype`          (in)
+ *   o   [B, Hq,  Sq, d]  element type `dtype`          (out)
+ *   lse [B, Hq,  Sq]     float32, natural log          (out; may be NULL to skip)
+ *   scale: the score multiplier (1/sqrt(d) is the usual value); must be finite.
+ *   Sk = 0 is allowed: every row is empty (O = 0, LSE = -inf).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             attn_dtype_t dtype, void* stream);
+
+/*
+ * attn_fwd_fp8 -- forward on E4M3FN operands with per-block descales.
+ * "M4.6 - FlashAttention-3/4 Hardware Pipelines", section 0x06 ("Derive Where Every
+ * Scale Must Enter"; "Why The Source Raises Softmax Probabilities By 2^8"):
+ *   S = scale * dQ_i * dK_j * (Q8 K8_j^T) before the row max;  u = 2^8 exp(S - m);
+ *   P8 = E4M3(u) (round to nearest even) feeds the P V product;  l sums unrounded u;
+ *   o += dV_j * (P8 V8_j) per K/V tile;  O = o / l;  LSE = m + ln l - 8 ln 2.
+ *
+ *   q8 [B,Hq,Sq,d], k8/v8 [B,Hkv,Sk,d]: E4M3FN bytes (OCP encoding, max 448)   (in)
+ *   q_scale [B,Hq,ceil(Sq/128)], k_scale/v_scale [B,Hkv,ceil(Sk/128)]: float32
+ *       descales, one per 128-row block of the row axis                        (in)
+ *   o   [B,Hq,Sq,d]: o_dtype ATTN_BF16 or ATTN_F32                             (out)
+ *   lse [B,Hq,Sq] float32 (may be NULL)                                        (out)
+ *   Only d = 128 and causal = 0 are supported in this release (ATTN_ERR_HEADDIM /
+ *   ATTN_ERR_ARG otherwise).  K/V tiles of attn_fp8_kv_tile() keys are visited in
+ *   ascending order, which fixes the frame in which each probability is rounded.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                 const float* q_scale, const float* k_scale, const float* v_scale,
+                 void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                 float scale, int causal, attn_dtype_t o_dtype, void* stream);
+
+/* K/V tile width (keys) of the fp8 forward's streaming loop. */
+int attn_fp8_kv_tile(void);
+
+/*
+ * attn_bwd -- backward of attn_fwd from its saved O and LSE.
+ * "M4.4 - FlashAttention-2 ...", section 0x06.1 (Algorithm 2): D = rowsum(dO * O);
+ * each workgroup owns one K/V column tile of one K/V head, recomputes
+ * P = exp(scale Q K^T - LSE) tile by tile for every query head of the group,
+ * forms dS = P * (dP - D), keeps dK/dV in registers (the group sum over the query
+ * heads sharing the K/V head is done in the owner, section 0x06E) and adds
+ * dQ contributions to a float32 accumulator with atomics (section 0x06.1F);
+ * a last pass scales and converts dQ.
+ *
+ *   q,o,dO [B,Hq,Sq,d] and k,v [B,Hkv,Sk,d]: element type `dtype`              (in)
+ *   lse [B,Hq,Sq] float32 as written by attn_fwd                              (in)
+ *   dq [B,Hq,Sq,d], dk/dv [B,Hkv,Sk,d]: element type `grad_dtype`
+ *       (ATTN_F32, ATTN_BF16 or ATTN_F16)                                      (out)
+ *   workspace: >= attn_bwd_workspace_size(...) bytes of device memory, any
+ *       content on entry (float32 dQ accumulator + D rows)                   (scratch)
+ *   Requires Sk >= 1.  Results of the atomic dQ sum are not bitwise repeatable.
+ */
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d);
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             attn_dtype_t dtype, attn_dtype_t grad_dtype,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_splitkv -- one new query per sequence against a K/V cache.
+ * "M4.4 - FlashAttention-2 ...", section 0x01 (Flash-Decoding splits the K/V axis
+ * into chunks, then reduces over chunks) and "M4.3 - IO-Aware Attention ...",
+ * sections 0x08B-0x08F (partial (m, l, u) states merge exactly in any order).
+ * Pass 1: one workgroup per (chunk, b, kv head) reads its K/V chunk once for all
+ * H_q/H_kv query heads of the group and writes one partial (m, l, u) per query head.
+ * Pass 2: per (b, query head) the partials are merged in one max frame, O = u / l,
+ * LSE = m + ln l.
+ *
+ *   q [B,Hq,1,d]; k_cache, v_cache [B,Hkv,Smax,d]: element type `dtype`        (in)
+ *   seqlens_k: device int32[B], 0 <= seqlens_k[b] <= Smax; sequence b attends to
+ *       keys [0, seqlens_k[b]) (a length of 0 gives O = 0, LSE = -inf)          (in)
+ *   o [B,Hq,1,d] element type `dtype`; lse [B,Hq,1] float32 (may be NULL)      (out)
+ *   chunk: keys per split, a positive multiple of 64 (256 is the usual value).
+ *   workspace: >= attn_decode_workspace_size(B, Hq, Smax, d, chunk) bytes     (scratch)
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int Smax, int d, int chunk);
+int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                        const int* seqlens_k, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
+                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * attn_tile_plan -- host-side view of the causal / tail tile iterator the kernels use.
+ * For query rows [q_begin, q_end) against S_k keys in tiles of `block_k`, writes the
+ * number of key tiles visited in ascending order (*n_visit) and the index of the
+ * first visited tile that needs an element mask (*first_masked; == *n_visit when none
+ * does).  Classification follows "M4.4 - FlashAttention-2 ...", section 0x05.1B
+ * (skipped iff k0 > q_end - 1 + delta, fully visible iff k1 - 1 <= q_begin + delta,
+ * delta = S_k - S_q).  Pure host code; returns ATTN_ERR_ARG / ATTN_ERR_NULL on bad
+ * arguments.
+ */
+int attn_tile_plan(int q_begin, int q_end, int Sq, int Sk, int block_k, int causal,
+                   int* n_visit, int* first_masked);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */
