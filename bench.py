@@ -1,0 +1,248 @@
+"""Benchmark of the exact tiled attention library on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only CONFIG] [--no-cpu] [--no-extra]
+
+A step is one call of the hot path on the headline workload, fp16 forward
+q,k,v [1,8,4096,64] non-causal (34.36 GFLOP per call).  Inputs are resident in HBM
+before the timed region; the region is bracketed by device synchronisation and
+timed with HIP events recorded on the stream the kernels are launched on.  The
+other workloads (causal GQA prefill forward + backward, split-KV decode, fp8
+forward) are timed the same way and reported under "configs".
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _time_launches(fn, steps, warmup, torch):
+    """Per-launch HIP-event durations (ms) plus the whole-region time (ms)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return per, region0.elapsed_time(region1)
+
+
+def _fwd_flops(B, Hq, Sq, Sk, d, causal):
+    f = 4.0 * B * Hq * Sq * Sk * d
+    return f / 2 if causal else f
+
+
+def bench_fwd(name, w, steps, warmup, torch, eta):
+    t, p = w.tensors, w.params
+    q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    fn = lambda: eta.attn_fwd(q, k, v, scale=p["scale"], causal=p["causal"], o=o, lse=lse)
+    per, region = _time_launches(fn, steps, warmup, torch)
+    flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
+    med = statistics.median(per)
+    return {"workload": name, "kernel": "fwd_kernel", "ms_median": med, "ms_region_per_step": region / steps,
+            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
+            "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}, (q, k, v, o, lse)
+
+
+def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta):
+    t, p = w.tensors, w.params
+    q, k, v, o, lse = fwd_bufs
+    do = t["do"].cuda()
+    ws = torch.empty(eta.bwd_workspace_size(p["B"], p["Hq"], p["Hkv"], p["Sq"], p["Sk"], p["d"]),
+                     dtype=torch.uint8, device="cuda")
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    fn = lambda: eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"],
+                              grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv)
+    per, region = _time_launches(fn, steps, warmup, torch)
+    flops = 2.5 * _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
+    med = statistics.median(per)
+    return {"workload": name, "kernel": "bwd (preprocess + main + convert)", "ms_median": med,
+            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
+            "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}
+
+
+def bench_decode(name, w, steps, warmup, torch, eta):
+    t, p = w.tensors, w.params
+    q, kc, vc = (t[n].cuda() for n in ("q", "k", "v"))
+    lens = t["seqlens"].cuda()
+    ws = torch.empty(eta.decode_workspace_size(p["B"], p["Hq"], p["Smax"], p["d"], p["chunk"]),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((p["B"], p["Hq"], 1), dtype=torch.float32, device="cuda")
+    fn = lambda: eta.attn_decode_splitkv(q, kc, vc, lens, scale=p["scale"], chunk=p["chunk"], workspace=ws,
+                                         o=o, lse=lse)
+    per, region = _time_launches(fn, steps, warmup, torch)
+    total_keys = int(t["seqlens"].sum())
+    kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
+    med = statistics.median(per)
+    return {"workload": name, "kernel": "decode split + merge", "ms_median": med,
+            "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
+            "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
+
+
+def bench_fp8(name, w, steps, warmup, torch, eta):
+    t, p = w.tensors, w.params
+    q8, k8, v8 = (t[n].cuda() for n in ("q8", "k8", "v8"))
+    qs, ks, vs = (t[n].cuda() for n in ("q_scale", "k_scale", "v_scale"))
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device="cuda")
+    fn = lambda: eta.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, scale=p["scale"], o=o, lse=lse)
+    per, region = _time_launches(fn, steps, warmup, torch)
+    flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], False)
+    med = statistics.median(per)
+    return {"workload": name, "kernel": "fp8_fwd_kernel", "ms_median": med,
+            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": "fp8_e4m3",
+            "peak": PEAK_TFLOPS["fp8"], "frac_of_bf16_peak": flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+            "samples_ms": [round(x, 5) for x in per]}
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The float64 oracle on host cores over whole heads of the headline workload
+    until ``budget_s`` is spent; throughput scaled to TFLOP/s."""
+    import numpy as np
+    from oracle import dense
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    t, p = w.tensors, w.params
+    heads = [(b, h) for b in range(p["B"]) for h in range(p["Hq"])]
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        dense.forward(t["q"], t["k"], t["v"], p["scale"], p["causal"], heads=[heads[done % len(heads)]])
+        done += 1
+    el = time.perf_counter() - t0
+    flops = _fwd_flops(1, done, p["Sq"], p["Sk"], p["d"], p["causal"])
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} (batch, head) passes of the headline workload ({len(heads)} pairs per call), "
+                      f"float64 numpy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None, help="run only this extra workload (c3, c4, c5)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the kernels run on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attn_inputs
+    import exact_tiled_attention_amd as eta
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    eta.lib()
+
+    head_name = "fp16 fwd q,k,v [1,8,4096,64] non-causal"
+    w2 = attn_inputs.CONFIGS["c2_fp16_fwd"]()
+    _log("[bench] headline", head_name)
+    head, _ = bench_fwd(head_name, w2, args.steps, args.warmup, torch, eta)
+
+    configs = {}
+    if not args.no_extra:
+        want = [args.only] if args.only else ["c3", "c4", "c5"]
+        if "c3" in want:
+            _log("[bench] c3 causal GQA prefill fwd + bwd")
+            w3 = attn_inputs.CONFIGS["c3_bf16_causal_gqa"]()
+            name = "bf16 causal GQA q [2,32,8192,128] k,v [2,8,8192,128]"
+            r, bufs = bench_fwd(name + " fwd", w3, max(5, args.steps // 3), 2, torch, eta)
+            configs["c3_fwd"] = r
+            try:
+                configs["c3_bwd"] = bench_bwd(name + " bwd", w3, bufs, max(3, args.steps // 5), 1, torch, eta)
+            except eta.AttnError as e:
+                configs["c3_bwd"] = {"error": str(e)}
+            del bufs, w3
+            torch.cuda.empty_cache()
+        if "c4" in want:
+            _log("[bench] c4 split-KV decode")
+            w4 = attn_inputs.CONFIGS["c4_bf16_decode"]()
+            try:
+                configs["c4_decode"] = bench_decode("bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768] chunk 256",
+                                                    w4, args.steps, args.warmup, torch, eta)
+            except eta.AttnError as e:
+                configs["c4_decode"] = {"error": str(e)}
+            del w4
+            torch.cuda.empty_cache()
+        if "c5" in want:
+            _log("[bench] c5 fp8 forward")
+            w5 = attn_inputs.CONFIGS["c5_fp8_fwd"]()
+            try:
+                configs["c5_fp8"] = bench_fp8("fp8 e4m3 fwd [4,16,8192,128] 128-row block scales, bf16 out",
+                                              w5, max(5, args.steps // 3), 2, torch, eta)
+            except eta.AttnError as e:
+                configs["c5_fp8"] = {"error": str(e)}
+            del w5
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        _log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(w2)
+
+    achieved = head["tflops"]
+    line = {
+        "metric": "attention fwd TFLOP/s (% of MFMA peak)",
+        "value": round(achieved, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_region_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": head_name, "B": 1, "H": 8, "S": 4096, "d": 64, "causal": False,
+                   "flops_per_step": head["flops_per_call"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f16"], 4), "traffic": None,
+                     "kernel": "fwd_kernel", "kernel_ms_median": round(head["ms_median"], 5)},
+        "cpu_baseline": cpu,
+        "configs": {k: {kk: vv for kk, vv in v.items() if kk != "samples_ms"} for k, v in configs.items()},
+        "samples_ms": head["samples_ms"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,6 +125,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (grad_dtype != ATTN_F32 && grad_dtype != ATTN_BF16 && grad_dtype != ATTN_F16)
     return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_ARG;
+  if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;   // one grid row per (b, kv head)
   const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   const size_t rows = (size_t)B * Hq * Sq;
@@ -162,6 +163,7 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (chunk <= 0 || chunk % 64 != 0 || chunk > 4096 || !isfinite(scale)) return ATTN_ERR_ARG;
+  if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;   // one grid row per (b, kv head)
   const size_t need = attn_decode_workspace_size(B, Hq, Smax, d, chunk);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   DecodeArgs a = {};

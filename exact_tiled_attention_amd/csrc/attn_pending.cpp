@@ -4,5 +4,3 @@
 
 hipError_t attn_launch_fwd_fp8(const Fp8Args&, hipStream_t) { return hipErrorNotSupported; }
 int attn_fp8_tile_keys() { return 64; }
-hipError_t attn_launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t attn_launch_decode(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }

@@ -40,3 +40,42 @@ ATTN_HD TilePlan plan_rows(int q0, int q1, int Sq, int Sk, int bk, int causal) {
   p.first_masked = full_tiles < p.n_visit ? full_tiles : p.n_visit;
   return p;
 }
+
+// Column view used by the backward's K/V-column owner: for the key tile [k0, k1)
+// (k1 <= S_k), the query tiles of height bq that see at least one of its keys are
+// first_qtile .. n_qtiles-1, and the ones before nomask_qtile intersect the causal
+// band (need an element mask).  A query row q sees key k iff k <= q + delta, so the
+// first row seeing key k0 is k0 - delta and the first row seeing every key of the
+// tile is (k1 - 1) - delta ("M4.4 - FlashAttention-2 ...", section 0x06.1G: causality
+// makes the producer set of each column triangular).
+struct ColPlan {
+  int first_qtile;
+  int nomask_qtile;
+  int n_qtiles;
+};
+
+ATTN_HD ColPlan plan_cols(int k0, int k1, int Sq, int Sk, int bq, int causal) {
+  ColPlan p;
+  p.n_qtiles = ceil_div_i(Sq, bq);
+  if (!causal) {
+    p.first_qtile = 0;
+    p.nomask_qtile = 0;
+    return p;
+  }
+  const int delta = Sk - Sq;
+  int first_row = k0 - delta;
+  if (first_row < 0) first_row = 0;
+  if (first_row >= Sq) {
+    p.first_qtile = p.n_qtiles;
+    p.nomask_qtile = p.n_qtiles;
+    return p;
+  }
+  p.first_qtile = first_row / bq;
+  int full_row = (k1 - 1) - delta;
+  if (full_row < 0) full_row = 0;
+  int nm = ceil_div_i(full_row, bq);
+  if (nm < p.first_qtile) nm = p.first_qtile;
+  if (nm > p.n_qtiles) nm = p.n_qtiles;
+  p.nomask_qtile = nm;
+  return p;
+}
