@@ -40,6 +40,12 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def _round_to(x, dtype):
+    """Round float64 values to a 16-bit storage type (torch's round-to-nearest-even)."""
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(dtype).double().numpy()
+
+
 def visible(sq: int, sk: int, causal: bool, rows=None) -> np.ndarray:
     """Boolean [len(rows), sk]: True where query row i may see key k."""
     rows = np.arange(sq) if rows is None else np.asarray(rows)
@@ -104,12 +110,18 @@ def probabilities(q, k, scale: float, causal: bool = False):
     return P
 
 
-def backward(q, k, v, do, scale: float, causal: bool = False, heads=None):
-    """Exact gradients of ``forward`` contracted with dO.
+def backward(q, k, v, do, scale: float, causal: bool = False, heads=None, o_storage=None):
+    """Gradients of ``forward`` contracted with dO.
 
     Returns (dQ [B,Hq,Sq,d], dK [B,Hkv,Sk,d], dV [B,Hkv,Sk,dv], D [B,Hq,Sq]) in float64.
     ``heads``: optional list of (b, h_kv) pairs; only their query groups are evaluated
     (the rest of dQ/dK/dV is NaN).
+
+    ``o_storage``: None gives the exact gradient (D = rowsum(P * dP)).  A torch dtype
+    (float16 / bfloat16) forms D = rowsum(dO * O_stored) from the forward output
+    rounded (to nearest even) to that storage type: the backward reads the O that the
+    forward wrote in the element type ([FA2] 0x03H: O is written in the input dtype;
+    0x06.1D: the preprocessing pass reads O and dO to form D).
     """
     Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(do)
     B, Hq, Sq, _ = Q.shape
@@ -129,7 +141,11 @@ def backward(q, k, v, do, scale: float, causal: bool = False, heads=None):
             _, _, P = _head_forward(Q[b, h], K[b, kv], V[b, kv], s, mask)
             dV[b, kv] += P.T @ dO[b, h]
             dP = dO[b, h] @ V[b, kv].T
-            D = (P * dP).sum(axis=1)
+            if o_storage is None:
+                D = (P * dP).sum(axis=1)
+            else:
+                O_st = _round_to(P @ V[b, kv], o_storage)
+                D = (dO[b, h] * O_st).sum(axis=1)
             dS = P * (dP - D[:, None])
             dQ[b, h] = s * (dS @ K[b, kv])
             dK[b, kv] += s * (dS.T @ Q[b, h])

@@ -85,3 +85,22 @@ def test_group_sum_example():
     _, dke, dve, _ = dense.backward(q, np.repeat(k, 3, 1), np.repeat(v, 3, 1), do, 0.7, True)
     assert np.allclose(dk, dke.reshape(1, 2, 3, 5, 3).sum(2), atol=1e-14)
     assert np.allclose(dv, dve.reshape(1, 2, 3, 5, 3).sum(2), atol=1e-14)
+
+
+def test_stored_output_D_reading():
+    """D from the output as stored in a 16-bit type: equal to the exact gradient when
+    the stored O is exact, and different by exactly the rounding term otherwise."""
+    q, k, do = _rand((1, 2, 6, 4), 21), _rand((1, 2, 6, 4), 22), _rand((1, 2, 6, 4), 23)
+    v = np.full((1, 2, 6, 4), 0.75)               # every O row is exactly 0.75
+    for dt in (torch.float16, torch.bfloat16):
+        exact = dense.backward(q, k, v, do, 0.5, True)
+        stored = dense.backward(q, k, v, do, 0.5, True, o_storage=dt)
+        for a, b in zip(exact, stored):
+            assert np.allclose(a, b, atol=1e-13)
+    v = _rand((1, 2, 6, 4), 24)
+    O, _ = dense.forward(q, k, v, 0.5, True)
+    _, _, _, D_exact = dense.backward(q, k, v, do, 0.5, True)
+    _, _, _, D_st = dense.backward(q, k, v, do, 0.5, True, o_storage=torch.bfloat16)
+    O_bf = torch.from_numpy(O).to(torch.bfloat16).double().numpy()
+    assert np.allclose(D_st - D_exact, (do * (O_bf - O)).sum(-1), atol=1e-13)
+    assert np.abs(D_st - D_exact).max() > 0
