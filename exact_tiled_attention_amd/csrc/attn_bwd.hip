@@ -78,6 +78,37 @@ __global__ __launch_bounds__(kNT) void bwd_convert_kernel(BwdArgs a, int64_t n4)
 
 template <typename G> __device__ inline void store_grad(G* p, float x) { *p = (G)x; }
 
+// bf16 keeps 8 significant bits; P and dS feed the dV / dK sums as hi + lo pairs.
+template <typename T> constexpr bool kSplit = false;
+template <> constexpr bool kSplit<bf16> = true;
+
+// Pack 8 floats into 8 element values (hi) and, for bf16, the 8 residuals x - hi (lo).
+template <typename T>
+__device__ inline void split_pack8(const f32x16& x, int off, u32x4& hi, u32x4& lo) {
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = x[off + j];
+  hi.x = Elem<T>::pack2(r[0], r[1]);
+  hi.y = Elem<T>::pack2(r[2], r[3]);
+  hi.z = Elem<T>::pack2(r[4], r[5]);
+  hi.w = Elem<T>::pack2(r[6], r[7]);
+  if (kSplit<T>) {
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t hw = hi[j];
+      e[2 * j] = r[2 * j] - __builtin_bit_cast(float, hw << 16);
+      e[2 * j + 1] = r[2 * j + 1] - __builtin_bit_cast(float, hw & 0xFFFF0000u);
+    }
+    lo.x = Elem<T>::pack2(e[0], e[1]);
+    lo.y = Elem<T>::pack2(e[2], e[3]);
+    lo.z = Elem<T>::pack2(e[4], e[5]);
+    lo.w = Elem<T>::pack2(e[6], e[7]);
+  } else {
+    lo = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // 2. main column-owner kernel
 template <int D, int BQ>
@@ -279,21 +310,17 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     }
     // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries
     // 16c + 8(j/4) + 4g + j%4 (registers 8(c%2) + j of query block c/2).
+    // With bf16 elements P and dS enter as hi + lo pairs of bf16 values (x = hi + lo
+    // to about 16 significant bits), so these two sums keep float32-like precision.
     const T* sqt = lds + L::QT;
     const T* sdot = lds + L::DOT;
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
       const int mb = c >> 1;
       const int hb = (c & 1) * 8;
-      u32x4 pp, ss;
-      pp.x = E::pack2(s[mb][hb + 0], s[mb][hb + 1]);
-      pp.y = E::pack2(s[mb][hb + 2], s[mb][hb + 3]);
-      pp.z = E::pack2(s[mb][hb + 4], s[mb][hb + 5]);
-      pp.w = E::pack2(s[mb][hb + 6], s[mb][hb + 7]);
-      ss.x = E::pack2(dp[mb][hb + 0], dp[mb][hb + 1]);
-      ss.y = E::pack2(dp[mb][hb + 2], dp[mb][hb + 3]);
-      ss.z = E::pack2(dp[mb][hb + 4], dp[mb][hb + 5]);
-      ss.w = E::pack2(dp[mb][hb + 6], dp[mb][hb + 7]);
+      u32x4 pp, ss, pl, sl;
+      split_pack8<T>(s[mb], hb, pp, pl);
+      split_pack8<T>(dp[mb], hb, ss, sl);
       const V8 pa = as_v8<V8>(pp);
       const V8 sa = as_v8<V8>(ss);
 #pragma unroll
@@ -307,6 +334,10 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
         const u32x4 qb4 = {qlo.x, qlo.y, qhi.x, qhi.y};
         dv[db] = E::mfma(pa, as_v8<V8>(ob), dv[db]);
         dk[db] = E::mfma(sa, as_v8<V8>(qb4), dk[db]);
+        if (kSplit<T>) {
+          dv[db] = E::mfma(as_v8<V8>(pl), as_v8<V8>(ob), dv[db]);
+          dk[db] = E::mfma(as_v8<V8>(sl), as_v8<V8>(qb4), dk[db]);
+        }
       }
     }
     // dS -> LDS as [query][key] (16-bit) for the dQ product.
