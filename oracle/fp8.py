@@ -74,8 +74,23 @@ def round_e4m3(x) -> np.ndarray:
     return _TABLE[encode_rne_sat(x)]
 
 
+def rounding_alternative(u, rel: float):
+    """For each u >= 0: the other E4M3 neighbour when u lies within ``rel * u`` of the
+    midpoint between its two neighbours (the rounding is then not decided by float32
+    arithmetic of that accuracy), else the rounded value itself."""
+    u = np.minimum(np.asarray(u, dtype=np.float64), E4M3_MAX)
+    hi = np.minimum(np.searchsorted(_POS_VALUES, u, side="left"), len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    vlo, vhi = _POS_VALUES[lo], _POS_VALUES[hi]
+    mid = 0.5 * (vlo + vhi)
+    near = (vhi > vlo) & (np.abs(u - mid) <= rel * u)
+    r = _TABLE[encode_rne_sat(u)]
+    return np.where(near, np.where(r == vlo, vhi, vlo), r)
+
+
 def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 64,
-            scale_rows: int = 128, rows=None, heads=None, prob_round=round_e4m3, frame="running"):
+            scale_rows: int = 128, rows=None, heads=None, prob_round=round_e4m3, frame="running",
+            envelope_rel=None):
     """The quantised forward, step by step (non-causal).
 
     q8/k8/v8: E4M3FN codes [B,H,S,d] (uint8); *_scale: float32 [B,H,ceil(S/128)].
@@ -83,7 +98,11 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
     ``prob_round``: the probability rounding (identity removes it).
     ``frame``: "running" rounds u in the running-max frame (the kernel's order);
     "final" rounds it in the final row-max frame (an informational variant).
-    Returns (O [B,Hq,R,d], LSE [B,Hq,R]) in float64.
+    ``envelope_rel``: when set, also return E [B,Hq,R,d], the largest change of O that
+    flipping every probability whose rounding lies within ``envelope_rel`` (relative)
+    of an E4M3 midpoint could cause: u is specified in float32, so such a rounding is
+    not determined by the method's own arithmetic and either neighbour is correct.
+    Returns (O [B,Hq,R,d], LSE [B,Hq,R]) in float64 (and E).
     """
     assert scale_rows % block_c == 0, "a K/V tile must lie inside one scale block"
     Q, K, V = decode(q8), decode(k8), decode(v8)
@@ -97,6 +116,7 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
     LSE = np.full((B, Hq, len(rows)), np.nan)
     pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
     off = float(2 ** PROB_OFFSET_LOG2)
+    E = np.full_like(O, np.nan) if envelope_rel is not None else None
     for b, h in pairs:
         kv = h // g
         Qi = Q[b, h][rows]
@@ -107,6 +127,7 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
         m = np.full(len(rows), -np.inf)
         l = np.zeros(len(rows))
         o = np.zeros((len(rows), V.shape[3]))
+        e = np.zeros((len(rows), V.shape[3]))
         for k0 in range(0, Sk, block_c):
             k1 = min(Sk, k0 + block_c)
             dk = ks[b, kv][k0 // scale_rows]
@@ -123,9 +144,16 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
                 p8 = prob_round(u)
             l = alpha * l + u.sum(axis=1)
             o = alpha[:, None] * o + dv * (p8 @ V[b, kv][k0:k1])
+            if envelope_rel is not None:
+                flip = np.abs(rounding_alternative(u, envelope_rel) - p8)
+                e = alpha[:, None] * e + dv * (flip @ np.abs(V[b, kv][k0:k1]))
             m = m_new
         O[b, h] = o / l[:, None]
         LSE[b, h] = m + np.log(l) - PROB_OFFSET_LOG2 * math.log(2.0)
+        if E is not None:
+            E[b, h] = e / l[:, None]
+    if E is not None:
+        return O, LSE, E
     return O, LSE
 
 

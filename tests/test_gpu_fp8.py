@@ -1,0 +1,78 @@
+"""GPU parity of attn_fwd_fp8 against the oracle's step-by-step quantised forward."""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+from oracle import dense, fp8
+from gpu_common import TOL_FP8, assert_close_lse, assert_close_out, need_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# Relative distance to an E4M3 midpoint below which a float32 probability's rounding is
+# treated as undecided: the kernel's u carries a relative error of about
+# ln2 * 2^-24 * (|score| + |max|) in base-2 units, below 2^-12 for |score| < 2^10.
+AMBIGUITY_REL = 2.0 ** -12
+
+
+def _gpu(w, o_dtype):
+    import exact_tiled_attention_amd as eta
+    t, p = w.tensors, w.params
+    args = [to_dev(t[n]) for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale")]
+    o, lse = eta.attn_fwd_fp8(*args, scale=p["scale"], o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _check(w, rows=None, heads=None):
+    import exact_tiled_attention_amd as eta
+    t, p = w.tensors, w.params
+    tile = eta.fp8_kv_tile()
+    say(f"[fp8] {w.name} tile={tile}")
+    o32, l32 = _gpu(w, torch.float32)
+    obf, lbf = _gpu(w, torch.bfloat16)
+    # the bf16 output is the round-to-nearest-even of the float32 result
+    assert torch.equal(obf, o32.to(torch.bfloat16)) and torch.equal(lbf, l32)
+    O, L, E = fp8.forward(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"], p["scale"],
+                          block_c=tile, rows=rows, heads=heads, envelope_rel=AMBIGUITY_REL)
+    if rows is not None:
+        o32, l32 = o32[:, :, rows], l32[:, :, rows]
+    if heads is not None:
+        sel = tuple(np.array(heads).T)
+        o32, l32, O, L, E = o32[sel], l32[sel], O[sel], L[sel], E[sel]
+    # 5e-2 plus, per element, what E4M3 roundings left undecided by float32 scores
+    # could move the output (either neighbour is a correct rounding there)
+    err = np.abs(o32.double().numpy() - O)
+    bad = err > TOL_FP8 + E
+    assert not bad.any(), f"{w.name}: max err {err.max():.3e} at {np.argwhere(bad)[:5].tolist()}"
+    e1 = float(err.max())
+    say(f"    elements whose bound was widened by ambiguous roundings: {(E > 0).mean():.2%}, max E {E.max():.3e}")
+    e2 = assert_close_lse(l32, L, w.name)
+    # informational: error of the quantised path against dense attention on the
+    # dequantised inputs (the FA3 accuracy table reports RMSE against float64)
+    Od, _ = dense.forward(fp8.dequantized(t["q8"], t["q_scale"]), fp8.dequantized(t["k8"], t["k_scale"]),
+                          fp8.dequantized(t["v8"], t["v_scale"]), p["scale"], False, rows=rows, heads=heads)
+    if heads is not None:
+        Od = Od[sel]
+    rmse = float(np.sqrt(np.mean((o32.double().numpy() - Od) ** 2)))
+    say(f"    max|dO| vs oracle {e1:.2e}, max|dLSE| {e2:.2e}, RMSE vs unquantised P {rmse:.3e}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk", [(1, 2, 2, 128, 128), (2, 4, 2, 200, 333), (1, 2, 1, 64, 1), (1, 1, 1, 300, 64)])
+def test_fp8_small_elementwise(B, Hq, Hkv, Sq, Sk):
+    need_gpu()
+    _check(attn_inputs.fp8_prefill(B, Hq, Hkv, Sq, Sk, 128, seed=500 + Sq + Sk))
+
+
+def test_fp8_config5_full_size_sampled():
+    need_gpu()
+    w = attn_inputs.CONFIGS["c5_fp8_fwd"]()
+    rows = np.unique(np.concatenate([np.arange(0, 8192, 331), [0, 127, 128, 8191]]))
+    _check(w, rows=rows, heads=[(0, 0), (1, 7), (3, 15)])
+
+
+def test_fp8_bitwise_repeatable():
+    need_gpu()
+    w = attn_inputs.fp8_prefill(1, 4, 4, 512, 512, 128, seed=9)
+    a, b = _gpu(w, torch.bfloat16), _gpu(w, torch.bfloat16)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -93,3 +93,27 @@ def test_descales_enter_before_the_row_max():
     O_wrong, _ = fp8.forward(t["q8"], t["k8"], t["v8"], ones(t["q_scale"]), ones(t["k_scale"]), t["v_scale"],
                              p["scale"], prob_round=lambda u: u)
     assert np.abs(O_right - O_wrong).max() > 1e-2
+
+
+def test_rounding_alternative_band():
+    vals = fp8._POS_VALUES
+    mids = 0.5 * (vals[1:-1] + vals[2:])
+    alt = fp8.rounding_alternative(mids, 1e-6)
+    rn = fp8.round_e4m3(mids)
+    assert np.all(alt != rn)                                    # exact midpoints: both neighbours
+    far = 0.5 * (vals[1:-1] + mids)                             # a quarter-step from a value
+    assert np.array_equal(fp8.rounding_alternative(far, 1e-6), fp8.round_e4m3(far))
+
+
+def test_envelope_is_zero_without_ambiguity_and_bounds_a_flip():
+    w = _small_inputs(seed=17, S=128, d=32)
+    t, p = w.tensors, w.params
+    args = (t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"], p["scale"])
+    O, L = fp8.forward(*args, block_c=64)
+    O0, L0, E0 = fp8.forward(*args, block_c=64, envelope_rel=0.0)
+    assert np.array_equal(O, O0) and np.all(E0 == 0)
+    O1, _, E1 = fp8.forward(*args, block_c=64, envelope_rel=0.05)
+    # rounding every ambiguous probability the other way stays inside the envelope
+    Of, _ = fp8.forward(*args, block_c=64, prob_round=lambda u: fp8.rounding_alternative(u, 0.05))
+    assert np.all(np.abs(Of - O1) <= E1 + 1e-12)
+    assert E1.max() > 0
