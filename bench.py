@@ -29,6 +29,23 @@ PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_fp16_d64_1x8x4096_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter summary,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = dict(line.split(" = ", 1) for line in open(TRAFFIC_FILE).read().splitlines() if " = " in line)
+        src = open(os.path.join(ROOT, kv["kernel_source"].strip()), "rb").read()
+        if hashlib.sha256(src).hexdigest()[:16] != kv["kernel_source_sha256_16"].strip():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -159,6 +176,9 @@ def main():
     ap.add_argument("--only", default=None, help="run only this extra workload (c3, c4, c5)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="first run one 256 MiB device-to-device copy (known bytes) to calibrate "
+                         "the byte counters of a profiler run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -171,6 +191,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     eta.lib()
+
+    if args.copy_reference:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     head_name = "fp16 fwd q,k,v [1,8,4096,64] non-causal"
     w2 = attn_inputs.CONFIGS["c2_fp16_fwd"]()
@@ -235,7 +263,7 @@ def main():
         "config": {"workload": head_name, "B": 1, "H": 8, "S": 4096, "d": 64, "causal": False,
                    "flops_per_step": head["flops_per_call"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f16"],
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f16"], 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f16"], 4), "traffic": measured_traffic(),
                      "kernel": "fwd_kernel", "kernel_ms_median": round(head["ms_median"], 5)},
         "cpu_baseline": cpu,
         "configs": {k: {kk: vv for kk, vv in v.items() if kk != "samples_ms"} for k, v in configs.items()},

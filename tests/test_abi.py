@@ -1,0 +1,118 @@
+"""The C ABI: libattn.so loads without a GPU, exports every function include/attn.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import golden, ROOT
+
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _lib():
+    from exact_tiled_attention_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libattn.so not built (run __graft_entry__.build())")
+    return _lib.lib(), _lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib, mod = _lib()
+    names = _declared()
+    assert "attn_fwd" in names and "attn_bwd" in names and "attn_decode_splitkv" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mod.PROTOTYPES), "binding prototypes and header differ"
+
+
+def test_status_strings():
+    lib, _ = _lib()
+    for code in range(0, -9, -1):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(5) == b"unknown status"
+
+
+P = ctypes.c_void_p(16)   # a non-NULL placeholder: never dereferenced on rejected calls
+
+
+def test_fwd_argument_checks():
+    lib, _ = _lib()
+    f = lib.attn_fwd
+    ok = dict(B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=64)
+    def call(q=P, k=P, v=P, o=P, dtype=0, scale=0.125, **kw):
+        a = dict(ok, **kw)
+        return f(q, k, v, o, None, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], scale, 0, dtype, None)
+    assert call(q=None) == -1 and call(o=None) == -1 and call(k=None) == -1
+    assert call(B=0) == -2 and call(Sq=0) == -2 and call(Sk=-1) == -2 and call(Sq=1 << 21) == -2
+    assert call(Hq=3) == -3
+    assert call(d=96) == -4 and call(d=256) == -4
+    assert call(dtype=2) == -5 and call(dtype=3) == -5
+    assert call(scale=float("inf")) == -8 and call(scale=float("nan")) == -8
+
+
+def test_bwd_and_workspace_checks():
+    lib, _ = _lib()
+    ws = lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 64)
+    assert ws >= 1 * 4 * 8 * 64 * 4 + 1 * 4 * 8 * 4
+    assert lib.attn_bwd_workspace_size(1, 3, 2, 8, 8, 64) == 0
+    def call(ws_ptr=P, ws_bytes=ws, grad=2, **kw):
+        a = dict(B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=64, dtype=1)
+        a.update(kw)
+        return lib.attn_bwd(P, P, P, P, P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"],
+                            0.125, 1, a["dtype"], grad, ws_ptr, ws_bytes, None)
+    assert call(ws_ptr=None) == -6 and call(ws_bytes=ws - 1) == -6
+    assert call(grad=3) == -5 and call(dtype=2) == -5
+    assert call(Sk=0) == -2 and call(Hkv=3) == -3 and call(d=32) == -4
+    assert lib.attn_bwd(None, P, P, P, P, P, P, P, P, 1, 4, 2, 8, 8, 64, 0.125, 0, 1, 2, P, ws, None) == -1
+
+
+def test_decode_and_fp8_checks():
+    lib, _ = _lib()
+    ws = lib.attn_decode_workspace_size(2, 8, 512, 128, 256)
+    assert ws >= 2 * 8 * 2 * (128 + 2) * 4
+    assert lib.attn_decode_workspace_size(2, 8, 512, 128, 100) == 0
+    def dec(chunk=256, ws_bytes=ws, **kw):
+        a = dict(B=2, Hq=8, Hkv=2, Smax=512, d=128)
+        a.update(kw)
+        return lib.attn_decode_splitkv(P, P, P, P, P, None, a["B"], a["Hq"], a["Hkv"], a["Smax"], a["d"],
+                                       0.088, chunk, 1, P, ws_bytes, None)
+    assert dec(chunk=100) == -8 and dec(chunk=0) == -8 and dec(ws_bytes=ws - 1) == -6
+    assert dec(Hkv=3) == -3 and dec(d=80) == -4 and dec(Smax=0) == -2
+    assert lib.attn_fp8_kv_tile() in (32, 64, 128)
+    def f8(d=128, causal=0, odt=1, **kw):
+        a = dict(B=1, Hq=2, Hkv=2, Sq=8, Sk=8)
+        a.update(kw)
+        return lib.attn_fwd_fp8(P, P, P, P, P, P, P, None, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], d,
+                                0.088, causal, odt, None)
+    assert f8(d=64) == -4 and f8(causal=1) == -8 and f8(odt=0) == -5 and f8(Sk=0) == -2
+
+
+def test_tile_plan_matches_printed_causal_ledger():
+    """The kernels' tile iterator (exported host function) reproduces the printed
+    causal tile counts: visits and masked tiles per query tile."""
+    lib, _ = _lib()
+    n, fm = ctypes.c_int(), ctypes.c_int()
+    for c in golden("causal_tiles.json")["cases"]:
+        Sq, Sk, Br, Bc = c["Sq"], c["Sk"], c["Br"], c["Bc"]
+        visits, full = [], 0
+        for q0 in range(0, Sq, Br):
+            assert lib.attn_tile_plan(q0, min(Sq, q0 + Br), Sq, Sk, Bc, 1, ctypes.byref(n), ctypes.byref(fm)) == 0
+            visits.append(n.value)
+            full += fm.value
+        if "visited" in c:
+            assert sum(visits) == c["visited"]
+        if "visits_per_query_tile_first" in c:
+            assert visits[0] == c["visits_per_query_tile_first"] and visits[-1] == c["visits_per_query_tile_last"]
+        # tiles before first_masked are exactly the fully visible ones that need no tail mask
+        if Sk % Bc == 0:
+            assert full == c["full"]
+    assert lib.attn_tile_plan(0, 0, 8, 8, 64, 1, ctypes.byref(n), ctypes.byref(fm)) == -8
+    assert lib.attn_tile_plan(0, 8, 8, 8, 64, 1, None, ctypes.byref(fm)) == -1
