@@ -17,9 +17,17 @@
 // keys the S^T accumulator put in registers 8(c%2) .. 8(c%2)+7.  V^T therefore sits
 // in LDS transposed ([d][key]); the transpose happens on the way in, in registers.
 //
-// Exponentials run in base 2 with scale * log2(e) folded into the score scale.
+// Exponentials run in base 2: p = exp2(s * c - m) with c = scale * log2(e) in one FMA.
 // Masking (key tail and causal band) is applied before the row max, and only on the
-// tiles the tile plan marks (tile_plan.h).
+// tiles the tile plan marks (tile_plan.h).  Loads go through buffer resources whose
+// range check returns zeros past the tensor, so tails need no branches.
+//
+// Conditional rescale ("M4.6 - FlashAttention-3/4 Hardware Pipelines", section 0x09:
+// the reference maximum may stay stale while the new maximum exceeds it by at most a
+// threshold; numerator and denominator share that reference, so the result is exact):
+// the running max m moves only when some row of the wave sees a score more than
+// TAU = 8 (base 2) above it.  Otherwise alpha = 1 and the O / l rescale is skipped;
+// probabilities then stay below 2^8, well inside fp16 / bf16 range.
 #include "attn_device.h"
 #include "attn_launch.h"
 #include "tile_plan.h"
@@ -27,6 +35,7 @@
 namespace {
 
 constexpr int kWave = 64;
+constexpr float kTau = 8.f;   // conditional-rescale threshold, base-2 units
 
 template <int D, int BC>
 struct FwdLds {
@@ -39,7 +48,8 @@ struct FwdLds {
 };
 
 template <typename T, int D, int BC, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * kWave) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
   typedef FwdLds<D, BC> L;
@@ -69,9 +79,12 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(FwdArgs a) {
   const int h = bh - b * a.Hq;
   const int kvh = h / a.group;
 
-  const T* __restrict__ qb = reinterpret_cast<const T*>(a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
-  const T* __restrict__ kb = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const T* __restrict__ vb = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
+  const T* kb = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const T* vb = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, (uint32_t)a.Sq * D * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)a.Sk * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)a.Sk * D * 2);
 
   const int q0 = qt * BQ;
   const int q1 = min(q0 + BQ, a.Sq);
@@ -83,11 +96,18 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(FwdArgs a) {
   const int delta = a.Sk - a.Sq;
 
   // Q^T fragments (B operand): lane column = its query row, slots = d 16kc+8g .. +8.
+  // A negative score scale is moved into Q (sign flip) so that c >= 0 below and the
+  // row max can be taken on the raw accumulator values.
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float c = fabsf(a.scale_log2);
   V8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow < a.Sq) raw = ld_global_16(qb + (int64_t)qrow * D + 16 * kc + 8 * grp);
+    u32x4 raw = buf_load_16(qr, (uint32_t)(qrow * D + 16 * kc + 8 * grp) * 2);
+    raw.x ^= qsign;
+    raw.y ^= qsign;
+    raw.z ^= qsign;
+    raw.w ^= qsign;
     qf[kc] = as_v8<V8>(raw);
   }
 
@@ -107,22 +127,17 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(FwdArgs a) {
       const int idx = r * NT + tid;
       const int row = idx / (D / 8);
       const int c8 = idx % (D / 8);
-      const int key = k0 + row;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (idx < BC * D / 8 && key < a.Sk) val = ld_global_16(kb + (int64_t)key * D + c8 * 8);
-      kreg[r] = val;
+      kreg[r] = buf_load_16(kr, (uint32_t)((k0 + row) * D + c8 * 8) * 2);
     }
 #pragma unroll
     for (int r = 0; r < V_LOADS; ++r) {
       const int blk = r * NT + tid;
       const int kq = blk / (D / 8);
       const int dc = blk % (D / 8);
+      if (blk < V_BLOCKS) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = k0 + 4 * kq + s;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (blk < V_BLOCKS && key < a.Sk) val = ld_global_16(vb + (int64_t)key * D + dc * 8);
-        vreg[r][s] = val;
+        for (int s = 0; s < 4; ++s)
+          vreg[r][s] = buf_load_16(vr, (uint32_t)((k0 + 4 * kq + s) * D + dc * 8) * 2);
       }
     }
   };
@@ -175,42 +190,64 @@ __global__ __launch_bounds__(NW * kWave) void fwd_kernel(FwdArgs a) {
       }
     }
     const bool masked = t >= wplan.first_masked;
-    float mx = -INFINITY;
+    // Row max of c*s over this tile (c >= 0, so on the raw values).
+    float mx;
+    if (!masked) {
+      float r0 = s[0][0], r1 = s[0][1];
 #pragma unroll
-    for (int kbk = 0; kbk < KB; ++kbk) {
+      for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kbk][i] * a.scale_log2;
-        if (masked) {
+        for (int i = (kbk == 0 ? 2 : 0); i < 16; i += 2) {
+          r0 = fmaxf(r0, s[kbk][i]);
+          r1 = fmaxf(r1, s[kbk][i + 1]);
+        }
+      mx = fmaxf(r0, r1) * c;
+    } else {
+      float r0 = -INFINITY;
+#pragma unroll
+      for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
           const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
           const bool vis = key < a.Sk && (!CAUSAL || key <= qrow + delta);
-          x = vis ? x : -INFINITY;
+          s[kbk][i] = vis ? s[kbk][i] : -INFINITY;
+          r0 = fmaxf(r0, s[kbk][i]);
         }
-        s[kbk][i] = x;
-        mx = fmaxf(mx, x);
-      }
+      mx = r0 == -INFINITY ? -INFINITY : r0 * c;
     }
     mx = wave_max_xor32(mx);
-    const float m_new = fmaxf(m_i, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_i - m_use);
-    float rs = 0.f;
+    // Conditional rescale: move the reference only when some row needs it.
+    if (wave_any(mx > m_i + kTau)) {
+      const float m_new = fmaxf(m_i, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_i - m_new);
+      m_i = m_new;
+      l_i *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kbk = 0; kbk < KB; ++kbk) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(s[kbk][i] - m_use);
-        s[kbk][i] = pv;
-        rs += pv;
+      for (int i = 0; i < 16; i += 2) {
+        // masked cells hold -inf: exp2(-inf) = 0 (c > 0); c = 0 gives exp2(-m) = 1 for
+        // every visible cell, so masked cells are cleared explicitly in that path
+        float p0 = fast_exp2(fmaf(s[kbk][i], c, -m_use));
+        float p1 = fast_exp2(fmaf(s[kbk][i + 1], c, -m_use));
+        if (masked) {
+          p0 = s[kbk][i] == -INFINITY ? 0.f : p0;
+          p1 = s[kbk][i + 1] == -INFINITY ? 0.f : p1;
+        }
+        s[kbk][i] = p0;
+        s[kbk][i + 1] = p1;
+        rs0 += p0;
+        rs1 += p1;
       }
     }
-    l_i = alpha * l_i + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
+    l_i += rs0 + rs1;
 #pragma unroll
     for (int c = 0; c < PC; ++c) {
       const int kbk = c >> 1;
