@@ -47,14 +47,15 @@ struct FwdLds {
   static constexpr int BYTES = 2 * STAGE * 2;   // two stages of 16-bit elements
 };
 
-template <typename T, int D, int BC, int NW, bool CAUSAL>
+template <typename T, int D, int BC, int NW, int KS, bool CAUSAL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
   typedef FwdLds<D, BC> L;
-  constexpr int NT = NW * kWave;
-  constexpr int BQ = NW * 32;
+  constexpr int RB = NW / KS;                 // 32-row query blocks per workgroup
+  constexpr int NT = RB * kWave;              // threads staging one key range
+  constexpr int BQ = RB * 32;
   constexpr int KC = D / 16;                  // contraction chunks for S^T
   constexpr int KB = BC / 32;                 // key blocks of 32 per tile
   constexpr int DB = D / 32;                  // output d blocks of 32
@@ -63,13 +64,16 @@ void fwd_kernel(FwdArgs a) {
   constexpr int V_BLOCKS = (BC / 4) * (D / 8);          // 4-key x 8-d transpose blocks
   constexpr int V_LOADS = (V_BLOCKS + NT - 1) / NT;
 
-  __shared__ __attribute__((aligned(16))) T lds[2 * L::STAGE];
+  __shared__ __attribute__((aligned(16))) T lds_all[KS * 2 * L::STAGE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kh = wave / RB;                   // key range of this wave
+  const int w = wave % RB;                    // query block of this wave
+  const int tid = threadIdx.x % NT;           // index among the threads of this key range
   const int n = lane & 31;
   const int grp = lane >> 5;
+  T* lds = lds_all + kh * 2 * L::STAGE;
 
   const int BH = a.B * a.Hq;
   const int wg = blockIdx.x;
@@ -117,10 +121,11 @@ void fwd_kernel(FwdArgs a) {
   float m_i = -INFINITY;   // running max (base-2 units)
   float l_i = 0.f;         // this lane's share of the running denominator
 
-  u32x4 kreg[K_LOADS];
-  u32x4 vreg[V_LOADS][4];
+  // Two register sets: tile t+2 is in flight while tile t+1 waits to be stored.
+  u32x4 kreg2[2][K_LOADS];
+  u32x4 vreg2[2][V_LOADS][4];
 
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, u32x4 (&kreg)[K_LOADS], u32x4 (&vreg)[V_LOADS][4]) {
     const int k0 = t * BC;
 #pragma unroll
     for (int r = 0; r < K_LOADS; ++r) {
@@ -142,7 +147,7 @@ void fwd_kernel(FwdArgs a) {
     }
   };
 
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage, const u32x4 (&kreg)[K_LOADS], const u32x4 (&vreg)[V_LOADS][4]) {
     T* ks = lds + stage * L::STAGE;
     T* vs = ks + L::K_ELEMS;
 #pragma unroll
@@ -273,25 +278,72 @@ void fwd_kernel(FwdArgs a) {
     }
   };
 
+  // The visited tiles are split into KS contiguous ranges, one per group of RB waves.
+  // Software pipeline per range: at step i the LDS stage i%2 is read, tile i+1 (loaded
+  // one step earlier) is written to the other stage at the end, and tile i+2 is loaded
+  // into the register set that tile i occupied.  Every wave runs the same number of
+  // steps so the workgroup barriers line up.
   const int nt = plan.n_visit;
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
+  const int per = (nt + KS - 1) / KS;
+  const int tb = kh * per;
+  const int te = min(nt, tb + per);
+  if (tb < te) {
+    load_tile(tb, kreg2[0], vreg2[0]);
+    store_tile(0, kreg2[0], vreg2[0]);
   }
+  if (tb + 1 < te) load_tile(tb + 1, kreg2[1], vreg2[1]);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    if (t < wplan.n_visit) compute_tile(t, stage);
-    if (t + 1 < nt) store_tile(stage ^ 1);
+  for (int i = 0; i < per; i += 2) {
+    const int t = tb + i;
+    // even step: registers of set 0 are free, set 1 holds tile t+1
+    if (t + 2 < te) load_tile(t + 2, kreg2[0], vreg2[0]);
+    if (t < te && t < wplan.n_visit) compute_tile(t, 0);
+    if (t + 1 < te) store_tile(1, kreg2[1], vreg2[1]);
     __syncthreads();
+    if (i + 1 >= per) break;
+    // odd step: set 1 is free, set 0 holds tile t+2
+    if (t + 3 < te) load_tile(t + 3, kreg2[1], vreg2[1]);
+    if (t + 1 < te && t + 1 < wplan.n_visit) compute_tile(t + 1, 1);
+    if (t + 2 < te) store_tile(0, kreg2[0], vreg2[0]);
+    __syncthreads();
+  }
+
+  if (KS == 2) {
+    // Merge the two key ranges' states of each row in one max frame ("M4.3 -
+    // IO-Aware Attention ...", section 0x08B); the second range hands its (m, l, u)
+    // to the first through LDS.  Layout [block][value][lane] keeps lanes on banks.
+    constexpr int NV = 2 + 16 * DB;
+    float* xf = reinterpret_cast<float*>(lds_all);
+    float* mine = xf + (w * NV) * kWave + lane;
+    if (kh == 1) {
+      mine[0] = m_i;
+      mine[kWave] = l_i;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mine[(2 + 16 * db + i) * kWave] = o[db][i];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = mine[0];
+      const float l1 = mine[kWave];
+      const float m = fmaxf(m_i, m1);
+      const float a0 = (m == -INFINITY) ? 0.f : fast_exp2(m_i - m);
+      const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m1 - m);
+      l_i = a0 * l_i + a1 * l1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * mine[(2 + 16 * db + i) * kWave];
+      m_i = m;
+    }
   }
 
   // Epilogue: O = u / l once per row; LSE = (m + log2 l) ln 2 (FA2 section 0x02D).
   const float l_tot = l_i + __shfl_xor(l_i, 32);
   const bool empty = (m_i == -INFINITY) || !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
-  if (qrow < a.Sq) {
+  if (kh == 0 && qrow < a.Sq) {
     T* ob = reinterpret_cast<T*>(a.o) + ((int64_t)(b * a.Hq + h) * a.Sq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -309,24 +361,36 @@ void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int BC, int NW>
+template <typename T, int D, int BC, int NW, int KS>
 hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   FwdArgs a = a0;
-  constexpr int BQ = NW * 32;
+  constexpr int BQ = (NW / KS) * 32;
   a.nqt = (a.Sq + BQ - 1) / BQ;
   const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
   const dim3 block(NW * kWave);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, KS, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, KS, false>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+// Eight waves per workgroup.  When 256-row query tiles would leave fewer than two
+// workgroups per compute unit, the waves split into two groups that stream the two
+// halves of the K/V range for 128-row tiles instead (merged at the end).
+constexpr int kCUs = 256;
+
+template <typename T, int D>
+hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+  const int64_t wgs_full = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
+  if (wgs_full >= 2 * kCUs) return launch_fwd_t<T, D, 64, 8, 1>(a, stream);
+  return launch_fwd_t<T, D, 64, 8, 2>(a, stream);
 }
 
 template <typename T>
 hipError_t launch_fwd_dtype(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return launch_fwd_t<T, 64, 64, 4>(a, stream);
-  return launch_fwd_t<T, 128, 64, 4>(a, stream);
+  if (a.d == 64) return launch_fwd_d<T, 64>(a, stream);
+  return launch_fwd_d<T, 128>(a, stream);
 }
 
 }  // namespace
