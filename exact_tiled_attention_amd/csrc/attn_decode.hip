@@ -26,7 +26,10 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSub = 64;   // keys per wave per sub-tile
+#ifndef ATTN_DECODE_SUB
+#define ATTN_DECODE_SUB 64
+#endif
+constexpr int kSub = ATTN_DECODE_SUB;   // keys per wave per sub-tile
 
 template <typename T> struct Dot2;
 template <> struct Dot2<f16> {
@@ -232,15 +235,30 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int s = 1; s < 64; s <<= 1) M = fmaxf(M, __shfl_xor(M, s));
 
+  // Fold the partials in batches of 8 so that eight chunks' loads are in flight
+  // together (the fold itself is a short dependent chain).
+  constexpr int BATCH = 8;
   float L = 0.f;
   float U[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) U[j] = 0.f;
-  for (int cc = 0; cc < nch; ++cc) {
-    const float f = fast_exp2(ml[2 * cc] - M);
-    L += f * ml[2 * cc + 1];
+  for (int c0 = 0; c0 < nch; c0 += BATCH) {
+    float mv[BATCH], lv[BATCH], uv[BATCH][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) U[j] += f * pu[(int64_t)cc * D + lane + 64 * j];
+    for (int j = 0; j < BATCH; ++j) {
+      const int cc = min(c0 + j, nch - 1);
+      mv[j] = ml[2 * cc];
+      lv[j] = ml[2 * cc + 1];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) uv[j][q] = pu[(int64_t)cc * D + lane + 64 * q];
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const float f = (c0 + j < nch) ? fast_exp2(mv[j] - M) : 0.f;
+      L += f * lv[j];
+#pragma unroll
+      for (int q = 0; q < PER; ++q) U[q] += f * uv[j][q];
+    }
   }
   const bool empty = nch == 0 || !(L > 0.f);
   const float inv = empty ? 0.f : 1.f / L;
