@@ -2,9 +2,9 @@
 //
 // Schedule ("M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary",
 // section 0x03, Algorithm 1, and section 0x05C, split-Q): one workgroup owns one
-// query tile of one (batch, query head); each of its NW waves owns 32 disjoint query
-// rows, so no output is ever merged across waves.  The workgroup streams K/V tiles of
-// BC keys through a double-buffered LDS ring and every wave carries the online state
+// query tile of one (batch, query head); each wave owns 32 disjoint query rows, so no
+// output is merged across waves that share a key range.  The workgroup streams K/V
+// tiles of BC keys through an LDS ring and every wave carries the online state
 // (m, l, u) of its rows in registers ("M4.3 - IO-Aware Attention ...", section 0x09C;
 // FA2 section 0x02C: u <- alpha u + P~ V, normalised once at the end).
 //
@@ -14,13 +14,23 @@
 // per-lane scalars (one cross-lane exchange, lane l <-> l^32, for the max).  The
 // probabilities stay in registers and feed O^T += V^T P^T directly as the B operand:
 // slot j of lane group g in key chunk c is key 16c + 8(j/4) + 4g + j%4, the same
-// keys the S^T accumulator put in registers 8(c%2) .. 8(c%2)+7.  V^T therefore sits
-// in LDS transposed ([d][key]); the transpose happens on the way in, in registers.
+// keys the S^T accumulator put in registers 8(c%2) .. 8(c%2)+7.
+//
+// Staging.  K and V tiles are staged row-major in a two-slot LDS ring through one set
+// of registers: at step i every thread writes the tile it loaded at step i-1 into the
+// slot freed by the previous step, then loads tile i+2, then computes on tile i; one
+// workgroup barrier per step publishes the written tile and releases the slot read in
+// the step before.  The V^T operand of the P V product comes from ds_read_b64_tr_b16,
+// which hands each lane of a 16-lane group one column of a 4-row x 16-column block
+// (4 consecutive keys of one d), so V needs no transpose on the way in.  Rows are not
+// padded; each row's 16-byte chunks are XOR-swizzled instead (LDS chunk p of row r
+// holds global chunk p ^ swz(r)), with swizzles chosen so that the K reads, the V
+// transpose reads and the 16-byte tile writes all hit distinct banks.
 //
 // Exponentials run in base 2: p = exp2(s * c - m) with c = scale * log2(e) in one FMA.
 // Masking (key tail and causal band) is applied before the row max, and only on the
-// tiles the tile plan marks (tile_plan.h).  Loads go through buffer resources whose
-// range check returns zeros past the tensor, so tails need no branches.
+// tiles the tile plan marks (tile_plan.h).  Loads past the tensor return zeros (the
+// buffer range check), so tails need no branches.
 //
 // Conditional rescale ("M4.6 - FlashAttention-3/4 Hardware Pipelines", section 0x09:
 // the reference maximum may stay stale while the new maximum exceeds it by at most a
@@ -36,44 +46,53 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr float kTau = 8.f;   // conditional-rescale threshold, base-2 units
+constexpr int BC = 64;        // keys per K/V tile
 
-template <int D, int BC>
-struct FwdLds {
-  static constexpr int KSTR = D + 8;     // K row stride (elements): 16-byte pad
-  static constexpr int VSTR = BC + 4;    // V^T row stride (elements): 8-byte pad
-  static constexpr int K_ELEMS = BC * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * STAGE * 2;   // two stages of 16-bit elements
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Tile geometry for head dimension D: rows of D*2 bytes, CPR 16-byte chunks per row.
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int BYTES = BC * ROWB;          // one K or V tile
+  static constexpr int CHUNKS = BYTES / 16;        // 16-byte chunks per tile
+  // K: 16 consecutive rows must use 16 distinct bank groups for the b128 reads.
+  static __device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  // V: the 4 rows x 4 chunks read by one 32-lane pass of the transpose read must be
+  // 16 distinct bank groups.
+  static __device__ inline int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-template <typename T, int D, int BC, int NW, int KS, bool CAUSAL>
+template <typename T, int D, int NW, int KS, bool CAUSAL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
-  typedef FwdLds<D, BC> L;
+  typedef Tile<D> TL;
   constexpr int RB = NW / KS;                 // 32-row query blocks per workgroup
-  constexpr int NT = RB * kWave;              // threads staging one key range
   constexpr int BQ = RB * 32;
   constexpr int KC = D / 16;                  // contraction chunks for S^T
   constexpr int KB = BC / 32;                 // key blocks of 32 per tile
   constexpr int DB = D / 32;                  // output d blocks of 32
   constexpr int PC = BC / 16;                 // key chunks of 16 for P V
-  constexpr int K_LOADS = (BC * D / 8 + NT - 1) / NT;   // 16-byte K loads per thread
-  constexpr int V_BLOCKS = (BC / 4) * (D / 8);          // 4-key x 8-d transpose blocks
-  constexpr int V_LOADS = (V_BLOCKS + NT - 1) / NT;
+  constexpr int STAGE = 2 * TL::BYTES;        // K then V
+  constexpr int RING = 2 * STAGE;             // two slots
+  constexpr int NTK = RB * kWave;             // threads staging one key range
+  constexpr int LOADS = TL::CHUNKS / NTK;     // 16-byte K (and V) chunks per thread
+  static_assert(TL::CHUNKS % NTK == 0, "chunks must split evenly over the threads");
 
-  __shared__ __attribute__((aligned(16))) T lds_all[KS * 2 * L::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KS * RING];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kh = wave / RB;                   // key range of this wave
   const int w = wave % RB;                    // query block of this wave
-  const int tid = threadIdx.x % NT;           // index among the threads of this key range
   const int n = lane & 31;
   const int grp = lane >> 5;
-  T* lds = lds_all + kh * 2 * L::STAGE;
+  const int tid = threadIdx.x % NTK;          // index among the threads of this key range
+  uint8_t* ring = lds_all + kh * RING;
 
   const int BH = a.B * a.Hq;
   const int wg = blockIdx.x;
@@ -121,68 +140,33 @@ void fwd_kernel(FwdArgs a) {
   float m_i = -INFINITY;   // running max (base-2 units)
   float l_i = 0.f;         // this lane's share of the running denominator
 
-  // Two register sets: tile t+2 is in flight while tile t+1 waits to be stored.
-  u32x4 kreg2[2][K_LOADS];
-  u32x4 vreg2[2][V_LOADS][4];
-
-  auto load_tile = [&](int t, u32x4 (&kreg)[K_LOADS], u32x4 (&vreg)[V_LOADS][4]) {
-    const int k0 = t * BC;
+  // Staging: chunk idx = r * NTK + tid of a tile is LDS (row, pos) = (idx / CPR,
+  // idx % CPR) and holds global chunk pos ^ swz(row) of that row.
+  u32x4 kreg[LOADS], vreg[LOADS];
+  auto load_tile = [&](int t) {
 #pragma unroll
-    for (int r = 0; r < K_LOADS; ++r) {
-      const int idx = r * NT + tid;
-      const int row = idx / (D / 8);
-      const int c8 = idx % (D / 8);
-      kreg[r] = buf_load_16(kr, (uint32_t)((k0 + row) * D + c8 * 8) * 2);
+    for (int r = 0; r < LOADS; ++r) {
+      const int idx = r * NTK + tid;
+      const int row = idx / TL::CPR;
+      const int pos = idx % TL::CPR;
+      const uint32_t base = (uint32_t)((t * BC + row) * D) * 2;
+      kreg[r] = buf_load_16(kr, base + (uint32_t)((pos ^ TL::swz_k(row)) * 16));
+      vreg[r] = buf_load_16(vr, base + (uint32_t)((pos ^ TL::swz_v(row)) * 16));
     }
+  };
+  auto store_tile = [&](int slot) {
+    uint8_t* st = ring + slot * STAGE;
 #pragma unroll
-    for (int r = 0; r < V_LOADS; ++r) {
-      const int blk = r * NT + tid;
-      const int kq = blk / (D / 8);
-      const int dc = blk % (D / 8);
-      if (blk < V_BLOCKS) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          vreg[r][s] = buf_load_16(vr, (uint32_t)((k0 + 4 * kq + s) * D + dc * 8) * 2);
-      }
+    for (int r = 0; r < LOADS; ++r) {
+      const int idx = r * NTK + tid;
+      st_lds_16(st + idx * 16, kreg[r]);
+      st_lds_16(st + TL::BYTES + idx * 16, vreg[r]);
     }
   };
 
-  auto store_tile = [&](int stage, const u32x4 (&kreg)[K_LOADS], const u32x4 (&vreg)[V_LOADS][4]) {
-    T* ks = lds + stage * L::STAGE;
-    T* vs = ks + L::K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < K_LOADS; ++r) {
-      const int idx = r * NT + tid;
-      if (idx < BC * D / 8) {
-        const int row = idx / (D / 8);
-        const int c8 = idx % (D / 8);
-        st_lds_16(ks + row * L::KSTR + c8 * 8, kreg[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < V_LOADS; ++r) {
-      const int blk = r * NT + tid;
-      if (blk < V_BLOCKS) {
-        const int kq = blk / (D / 8);
-        const int dc = blk % (D / 8);
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          // dword wd of each of the 4 rows holds d columns 2wd and 2wd+1
-          u32x2 even, odd;
-          even.x = pack_lo(vreg[r][0][wd], vreg[r][1][wd]);
-          even.y = pack_lo(vreg[r][2][wd], vreg[r][3][wd]);
-          odd.x = pack_hi(vreg[r][0][wd], vreg[r][1][wd]);
-          odd.y = pack_hi(vreg[r][2][wd], vreg[r][3][wd]);
-          st_lds_8(vs + (dc * 8 + 2 * wd) * L::VSTR + 4 * kq, even);
-          st_lds_8(vs + (dc * 8 + 2 * wd + 1) * L::VSTR + 4 * kq, odd);
-        }
-      }
-    }
-  };
-
-  auto compute_tile = [&](int t, int stage) {
-    const T* ks = lds + stage * L::STAGE;
-    const T* vs = ks + L::K_ELEMS;
+  auto compute_tile = [&](int t, int slot) {
+    const uint8_t* ks = ring + slot * STAGE;
+    const uint8_t* vs = ks + TL::BYTES;
     f32x16 s[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) s[i] = f32x16{};
@@ -190,7 +174,9 @@ void fwd_kernel(FwdArgs a) {
     for (int kc = 0; kc < KC; ++kc) {
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk) {
-        const V8 av = as_v8<V8>(ld_lds_16(ks + (kbk * 32 + n) * L::KSTR + 16 * kc + 8 * grp));
+        const int row = kbk * 32 + n;
+        const int chunk = (2 * kc + grp) ^ TL::swz_k(row);
+        const V8 av = as_v8<V8>(ld_lds_16(ks + row * TL::ROWB + chunk * 16));
         s[kbk] = E::mfma(av, qf[kc], s[kbk]);
       }
     }
@@ -253,66 +239,69 @@ void fwd_kernel(FwdArgs a) {
       }
     }
     l_i += rs0 + rs1;
+    // V^T operand by transpose reads: the 16-lane group G = lane/16 reads the 4 keys
+    // x 16 d block at keys 16c + 4g (+8 for slots 4..7), d = 32db + 16(G%2); lane s of
+    // the group addresses key row s/4, d columns 4(s%4) .. +3.
+    const int s16 = lane & 15;
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
 #pragma unroll
-    for (int c = 0; c < PC; ++c) {
-      const int kbk = c >> 1;
-      const int hb = (c & 1) * 8;
+    for (int cc = 0; cc < PC; ++cc) {
+      const int kbk = cc >> 1;
+      const int hb = (cc & 1) * 8;
       u32x4 pk;
       pk.x = E::pack2(s[kbk][hb + 0], s[kbk][hb + 1]);
       pk.y = E::pack2(s[kbk][hb + 2], s[kbk][hb + 3]);
       pk.z = E::pack2(s[kbk][hb + 4], s[kbk][hb + 5]);
       pk.w = E::pack2(s[kbk][hb + 6], s[kbk][hb + 7]);
       const V8 pb = as_v8<V8>(pk);
+      const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
+      const int r1 = r0 + 8;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const T* vrow = vs + (db * 32 + n) * L::VSTR + 16 * c + 4 * grp;
-        const u32x2 lo = ld_lds_8(vrow);
-        const u32x2 hi = ld_lds_8(vrow + 8);
-        u32x4 av4;
-        av4.x = lo.x;
-        av4.y = lo.y;
-        av4.z = hi.x;
-        av4.w = hi.y;
+        const int col = 32 * db + dsub;                 // multiple of 4: 8 bytes in one chunk
+        const int ch = col >> 3;
+        const int hf = (col & 7) * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + r0 * TL::ROWB + ((ch ^ TL::swz_v(r0)) * 16) + hf));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + r1 * TL::ROWB + ((ch ^ TL::swz_v(r1)) * 16) + hf));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 av4 = {l2.x, l2.y, h2.x, h2.y};
         o[db] = E::mfma(as_v8<V8>(av4), pb, o[db]);
       }
     }
   };
 
   // The visited tiles are split into KS contiguous ranges, one per group of RB waves.
-  // Software pipeline per range: at step i the LDS stage i%2 is read, tile i+1 (loaded
-  // one step earlier) is written to the other stage at the end, and tile i+2 is loaded
-  // into the register set that tile i occupied.  Every wave runs the same number of
-  // steps so the workgroup barriers line up.
+  // Step i of a range: barrier (tile i, written during step i-1, is visible; the slot
+  // read at step i-1 is free), write tile i+1 from registers into that slot, load tile
+  // i+2 into the registers, compute tile i.  Every wave runs the same number of steps
+  // so the workgroup barriers line up.
   const int nt = plan.n_visit;
   const int per = (nt + KS - 1) / KS;
   const int tb = kh * per;
   const int te = min(nt, tb + per);
   if (tb < te) {
-    load_tile(tb, kreg2[0], vreg2[0]);
-    store_tile(0, kreg2[0], vreg2[0]);
+    load_tile(tb);
+    store_tile(0);
   }
-  if (tb + 1 < te) load_tile(tb + 1, kreg2[1], vreg2[1]);
-  __syncthreads();
-  for (int i = 0; i < per; i += 2) {
+  if (tb + 1 < te) load_tile(tb + 1);
+  for (int i = 0; i < per; ++i) {
     const int t = tb + i;
-    // even step: registers of set 0 are free, set 1 holds tile t+1
-    if (t + 2 < te) load_tile(t + 2, kreg2[0], vreg2[0]);
-    if (t < te && t < wplan.n_visit) compute_tile(t, 0);
-    if (t + 1 < te) store_tile(1, kreg2[1], vreg2[1]);
     __syncthreads();
-    if (i + 1 >= per) break;
-    // odd step: set 1 is free, set 0 holds tile t+2
-    if (t + 3 < te) load_tile(t + 3, kreg2[1], vreg2[1]);
-    if (t + 1 < te && t + 1 < wplan.n_visit) compute_tile(t + 1, 1);
-    if (t + 2 < te) store_tile(0, kreg2[0], vreg2[0]);
-    __syncthreads();
+    if (t + 1 < te) store_tile((i + 1) & 1);
+    if (t + 2 < te) load_tile(t + 2);
+    if (t < te && t < wplan.n_visit) compute_tile(t, i & 1);
   }
 
-  if (KS == 2) {
+  if constexpr (KS == 2) {
     // Merge the two key ranges' states of each row in one max frame ("M4.3 -
     // IO-Aware Attention ...", section 0x08B); the second range hands its (m, l, u)
     // to the first through LDS.  Layout [block][value][lane] keeps lanes on banks.
     constexpr int NV = 2 + 16 * DB;
+    static_assert(RB * NV * kWave * 4 <= KS * RING, "merge buffer fits in the ring");
+    __syncthreads();                                   // every wave is done with the ring
     float* xf = reinterpret_cast<float*>(lds_all);
     float* mine = xf + (w * NV) * kWave + lane;
     if (kh == 1) {
@@ -361,7 +350,7 @@ void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename T, int D, int BC, int NW, int KS>
+template <typename T, int D, int NW, int KS>
 hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   FwdArgs a = a0;
   constexpr int BQ = (NW / KS) * 32;
@@ -369,9 +358,9 @@ hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
   const dim3 block(NW * kWave);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, KS, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, KS, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, KS, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, KS, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -383,8 +372,8 @@ constexpr int kCUs = 256;
 template <typename T, int D>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
   const int64_t wgs_full = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
-  if (wgs_full >= 2 * kCUs) return launch_fwd_t<T, D, 64, 8, 1>(a, stream);
-  return launch_fwd_t<T, D, 64, 8, 2>(a, stream);
+  if (wgs_full >= 2 * kCUs) return launch_fwd_t<T, D, 8, 1>(a, stream);
+  return launch_fwd_t<T, D, 8, 2>(a, stream);
 }
 
 template <typename T>
