@@ -16,28 +16,39 @@
 // slot j of lane group g in key chunk c is key 16c + 8(j/4) + 4g + j%4, the same
 // keys the S^T accumulator put in registers 8(c%2) .. 8(c%2)+7.
 //
-// Staging.  K and V tiles are staged row-major in a two-slot LDS ring through one set
-// of registers: at step i every thread writes the tile it loaded at step i-1 into the
-// slot freed by the previous step, then loads tile i+2, then computes on tile i; one
-// workgroup barrier per step publishes the written tile and releases the slot read in
-// the step before.  The V^T operand of the P V product comes from ds_read_b64_tr_b16,
-// which hands each lane of a 16-lane group one column of a 4-row x 16-column block
-// (4 consecutive keys of one d), so V needs no transpose on the way in.  Rows are not
-// padded; each row's 16-byte chunks are XOR-swizzled instead (LDS chunk p of row r
-// holds global chunk p ^ swz(r)), with swizzles chosen so that the K reads, the V
-// transpose reads and the 16-byte tile writes all hit distinct banks.
+// Staging.  K and V tiles are staged row-major in LDS through registers, K and V in
+// rings of two slots each.  The V^T operand of the P V product comes from
+// ds_read_b64_tr_b16, which hands each lane of a 16-lane group one column of a 4-row
+// x 16-column block (4 consecutive keys of one d), so V needs no transpose on the way
+// in.  Rows are not padded; each row's 16-byte chunks are XOR-swizzled instead (LDS
+// chunk p of row r holds global chunk p ^ swz(r)), with swizzles chosen so that the
+// K reads, the V transpose reads and the 16-byte tile writes all hit distinct banks.
+//
+// Software pipeline.  Step t of a wave runs, chunk by chunk over the 16-key chunks
+// of the tile, the score product of tile t+1, the probabilities of tile t and the
+// P V product of tile t, so that each chunk's exponentials sit between matrix-core
+// instructions that do not depend on them; the row maximum of tile t+1 (and the
+// rescale decision) ends the step, under the tail of the P V product.  The rescale of
+// the output accumulator, when one is needed, follows the P V product of tile t,
+// whose terms still belong to the old maximum.  Staging runs one tile ahead: step t
+// writes K(t+2) and V(t+1) into LDS from registers, then loads K(t+3) and V(t+2) into
+// those registers; one workgroup barrier per step publishes the writes of the step
+// before and frees the slots read in it.
 //
 // Exponentials run in base 2: p = exp2(s * c - m) with c = scale * log2(e) in one FMA.
-// Masking (key tail and causal band) is applied before the row max, and only on the
-// tiles the tile plan marks (tile_plan.h).  Loads past the tensor return zeros (the
-// buffer range check), so tails need no branches.
+// Masking (key tail and causal band) sets the invisible scores to -inf before the row
+// max, and only on the tiles the tile plan marks (tile_plan.h); a zero scale uses the
+// smallest c that keeps c * (-inf) = -inf while c * s rounds to 0 for finite s.  Loads
+// past the tensor return zeros (the buffer range check), so tails need no branches.
 //
 // Conditional rescale ("M4.6 - FlashAttention-3/4 Hardware Pipelines", section 0x09:
 // the reference maximum may stay stale while the new maximum exceeds it by at most a
 // threshold; numerator and denominator share that reference, so the result is exact):
 // the running max m moves only when some row of the wave sees a score more than
 // TAU = 8 (base 2) above it.  Otherwise alpha = 1 and the O / l rescale is skipped;
-// probabilities then stay below 2^8, well inside fp16 / bf16 range.
+// probabilities then stay below 2^8, well inside fp16 / bf16 range.  The denominator
+// sums the fp32 probabilities (before their rounding to the element type), which
+// keeps the log-sum-exp at fp32 accuracy.
 #include "attn_device.h"
 #include "attn_launch.h"
 #include "tile_plan.h"
@@ -65,6 +76,16 @@ struct Tile {
   static __device__ inline int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// Maximum for scores: no NaN can occur, and the NaN-propagating form maps to
+// v_maximum3_f32 without operand canonicalisation.
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max over the two lanes l and l ^ 32 (one VALU lane swap).
+__device__ inline float max_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <typename T, int D, int NW, int KS, bool CAUSAL>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
@@ -77,8 +98,7 @@ void fwd_kernel(FwdArgs a) {
   constexpr int KB = BC / 32;                 // key blocks of 32 per tile
   constexpr int DB = D / 32;                  // output d blocks of 32
   constexpr int PC = BC / 16;                 // key chunks of 16 for P V
-  constexpr int STAGE = 2 * TL::BYTES;        // K then V
-  constexpr int RING = 2 * STAGE;             // two slots
+  constexpr int RING = 4 * TL::BYTES;         // K slots 0, 1 then V slots 0, 1
   constexpr int NTK = RB * kWave;             // threads staging one key range
   constexpr int LOADS = TL::CHUNKS / NTK;     // 16-byte K (and V) chunks per thread
   static_assert(TL::CHUNKS % NTK == 0, "chunks must split evenly over the threads");
@@ -92,7 +112,8 @@ void fwd_kernel(FwdArgs a) {
   const int n = lane & 31;
   const int grp = lane >> 5;
   const int tid = threadIdx.x % NTK;          // index among the threads of this key range
-  uint8_t* ring = lds_all + kh * RING;
+  uint8_t* kring = lds_all + kh * RING;
+  uint8_t* vring = kring + 2 * TL::BYTES;
 
   const int BH = a.B * a.Hq;
   const int wg = blockIdx.x;
@@ -116,13 +137,14 @@ void fwd_kernel(FwdArgs a) {
   const int w0 = q0 + w * 32;
   const int w1 = max(min(w0 + 32, a.Sq), w0 + 1);
   const TilePlan wplan = plan_rows(w0, w1, a.Sq, a.Sk, BC, CAUSAL);
-  const int delta = a.Sk - a.Sq;
+  // keys at or past klim are invisible to this lane's query row
+  const int klim = CAUSAL ? min(a.Sk, qrow + (a.Sk - a.Sq) + 1) : a.Sk;
 
   // Q^T fragments (B operand): lane column = its query row, slots = d 16kc+8g .. +8.
-  // A negative score scale is moved into Q (sign flip) so that c >= 0 below and the
+  // A negative score scale is moved into Q (sign flip) so that c > 0 below and the
   // row max can be taken on the raw accumulator values.
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-  const float c = fabsf(a.scale_log2);
+  const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
   V8 qf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
@@ -143,156 +165,200 @@ void fwd_kernel(FwdArgs a) {
   // Staging: chunk idx = r * NTK + tid of a tile is LDS (row, pos) = (idx / CPR,
   // idx % CPR) and holds global chunk pos ^ swz(row) of that row.
   u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int t) {
+  auto load_k = [&](int t) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
       const int idx = r * NTK + tid;
       const int row = idx / TL::CPR;
       const int pos = idx % TL::CPR;
-      const uint32_t base = (uint32_t)((t * BC + row) * D) * 2;
-      kreg[r] = buf_load_16(kr, base + (uint32_t)((pos ^ TL::swz_k(row)) * 16));
-      vreg[r] = buf_load_16(vr, base + (uint32_t)((pos ^ TL::swz_v(row)) * 16));
+      kreg[r] = buf_load_16(kr, (uint32_t)((t * BC + row) * D) * 2 + (uint32_t)((pos ^ TL::swz_k(row)) * 16));
     }
   };
-  auto store_tile = [&](int slot) {
-    uint8_t* st = ring + slot * STAGE;
+  auto load_v = [&](int t) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
       const int idx = r * NTK + tid;
-      st_lds_16(st + idx * 16, kreg[r]);
-      st_lds_16(st + TL::BYTES + idx * 16, vreg[r]);
+      const int row = idx / TL::CPR;
+      const int pos = idx % TL::CPR;
+      vreg[r] = buf_load_16(vr, (uint32_t)((t * BC + row) * D) * 2 + (uint32_t)((pos ^ TL::swz_v(row)) * 16));
     }
   };
+  auto store_k = [&](int slot) {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) st_lds_16(kring + slot * TL::BYTES + (r * NTK + tid) * 16, kreg[r]);
+  };
+  auto store_v = [&](int slot) {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) st_lds_16(vring + slot * TL::BYTES + (r * NTK + tid) * 16, vreg[r]);
+  };
 
-  auto compute_tile = [&](int t, int slot) {
-    const uint8_t* ks = ring + slot * STAGE;
-    const uint8_t* vs = ks + TL::BYTES;
-    f32x16 s[KB];
+  // S^T MFMAs for contraction chunks [kc0, kc1) of one tile from K slot `slot`; the
+  // chunk kc = 0 starts from a zero accumulator.
+  auto score_part = [&](f32x16 (&sc)[KB], int slot, int kc0, int kc1) {
+    const uint8_t* ks = kring + slot * TL::BYTES;
 #pragma unroll
-    for (int i = 0; i < KB; ++i) s[i] = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
+    for (int kc = kc0; kc < kc1; ++kc) {
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk) {
         const int row = kbk * 32 + n;
         const int chunk = (2 * kc + grp) ^ TL::swz_k(row);
         const V8 av = as_v8<V8>(ld_lds_16(ks + row * TL::ROWB + chunk * 16));
-        s[kbk] = E::mfma(av, qf[kc], s[kbk]);
+        sc[kbk] = E::mfma(av, qf[kc], kc == 0 ? f32x16{} : sc[kbk]);
       }
     }
-    const bool masked = t >= wplan.first_masked;
-    // Row max of c*s over this tile (c >= 0, so on the raw values).
-    float mx;
-    if (!masked) {
-      float r0 = s[0][0], r1 = s[0][1];
+  };
+
+  // O^T += V^T P^T for key chunk cc from V slot `slot`.  The 16-lane group G =
+  // lane/16 reads the 4 keys x 16 d block at keys 16cc + 4g (+8 for slots 4..7),
+  // d = 32db + 16(G%2); lane s of the group addresses key row s/4, d columns
+  // 4(s%4) .. +3.
+  const int s16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+  auto pv_chunk = [&](const u32x4& p, int slot, int cc) {
+    const uint8_t* vs = vring + slot * TL::BYTES;
+    const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
+    const int r1 = r0 + 8;
 #pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + dsub;                 // multiple of 4: 8 bytes in one chunk
+      const int ch = col >> 3;
+      const int hf = (col & 7) * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vs + r0 * TL::ROWB + ((ch ^ TL::swz_v(r0)) * 16) + hf));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vs + r1 * TL::ROWB + ((ch ^ TL::swz_v(r1)) * 16) + hf));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 av4 = {l2.x, l2.y, h2.x, h2.y};
+      o[db] = E::mfma(as_v8<V8>(av4), as_v8<V8>(p), o[db]);
+    }
+  };
+
+  // Probabilities of key chunk cc of a scored tile, packed to the element type
+  // (slot j of lane group g = key 16cc + 8(j/4) + 4g + j%4, accumulator registers
+  // 8(cc%2) .. +7 of key block cc/2); their fp32 sum goes to l.
+  auto probs_chunk = [&](const f32x16 (&sc)[KB], int cc, float m_use, float& l0, float& l1) -> u32x4 {
+    const int kbk = cc >> 1;
+    const int hb = (cc & 1) * 8;
+    uint32_t pk[4];
 #pragma unroll
-        for (int i = (kbk == 0 ? 2 : 0); i < 16; i += 2) {
-          r0 = fmaxf(r0, s[kbk][i]);
-          r1 = fmaxf(r1, s[kbk][i + 1]);
-        }
-      mx = fmaxf(r0, r1) * c;
-    } else {
-      float r0 = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const float e0 = fast_exp2(fmaf(sc[kbk][hb + 2 * j], c, -m_use));
+      const float e1 = fast_exp2(fmaf(sc[kbk][hb + 2 * j + 1], c, -m_use));
+      l0 += e0;
+      l1 += e1;
+      pk[j] = E::pack2(e0, e1);
+    }
+    return u32x4{pk[0], pk[1], pk[2], pk[3]};
+  };
+
+  // Row max of tile t and the rescale decision; l is rescaled here, O by the caller
+  // (after the pending P V product).
+  auto row_max = [&](f32x16 (&sc)[KB], int t, bool& moved) -> float {
+    if (t >= wplan.first_masked) {
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
-          const bool vis = key < a.Sk && (!CAUSAL || key <= qrow + delta);
-          s[kbk][i] = vis ? s[kbk][i] : -INFINITY;
-          r0 = fmaxf(r0, s[kbk][i]);
+          sc[kbk][i] = key < klim ? sc[kbk][i] : -INFINITY;
         }
-      mx = r0 == -INFINITY ? -INFINITY : r0 * c;
     }
-    mx = wave_max_xor32(mx);
-    // Conditional rescale: move the reference only when some row needs it.
-    if (wave_any(mx > m_i + kTau)) {
+    float r0 = vmax(sc[0][0], sc[0][1]), r1 = vmax(sc[0][2], sc[0][3]);
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+      for (int i = (kbk == 0 ? 4 : 0); i < 16; i += 4) {
+        r0 = vmax(r0, vmax(sc[kbk][i], sc[kbk][i + 1]));
+        r1 = vmax(r1, vmax(sc[kbk][i + 2], sc[kbk][i + 3]));
+      }
+    const float mx = max_pair32(vmax(r0, r1) * c);
+    moved = wave_any(mx > m_i + kTau);
+    float alpha = 1.f;
+    if (moved) {
       const float m_new = fmaxf(m_i, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_i - m_new);
+      // the decision is per wave: a row with nothing visible yet keeps m = -inf, alpha 1
+      alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_i - m_new);
       m_i = m_new;
       l_i *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
-    const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
-    float rs0 = 0.f, rs1 = 0.f;
+    return alpha;
+  };
+  auto rescale_o = [&](float alpha) {
 #pragma unroll
-    for (int kbk = 0; kbk < KB; ++kbk) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        // masked cells hold -inf: exp2(-inf) = 0 (c > 0); c = 0 gives exp2(-m) = 1 for
-        // every visible cell, so masked cells are cleared explicitly in that path
-        float p0 = fast_exp2(fmaf(s[kbk][i], c, -m_use));
-        float p1 = fast_exp2(fmaf(s[kbk][i + 1], c, -m_use));
-        if (masked) {
-          p0 = s[kbk][i] == -INFINITY ? 0.f : p0;
-          p1 = s[kbk][i + 1] == -INFINITY ? 0.f : p1;
-        }
-        s[kbk][i] = p0;
-        s[kbk][i + 1] = p1;
-        rs0 += p0;
-        rs1 += p1;
-      }
-    }
-    l_i += rs0 + rs1;
-    // V^T operand by transpose reads: the 16-lane group G = lane/16 reads the 4 keys
-    // x 16 d block at keys 16c + 4g (+8 for slots 4..7), d = 32db + 16(G%2); lane s of
-    // the group addresses key row s/4, d columns 4(s%4) .. +3.
-    const int s16 = lane & 15;
-    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-#pragma unroll
-    for (int cc = 0; cc < PC; ++cc) {
-      const int kbk = cc >> 1;
-      const int hb = (cc & 1) * 8;
-      u32x4 pk;
-      pk.x = E::pack2(s[kbk][hb + 0], s[kbk][hb + 1]);
-      pk.y = E::pack2(s[kbk][hb + 2], s[kbk][hb + 3]);
-      pk.z = E::pack2(s[kbk][hb + 4], s[kbk][hb + 5]);
-      pk.w = E::pack2(s[kbk][hb + 6], s[kbk][hb + 7]);
-      const V8 pb = as_v8<V8>(pk);
-      const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
-      const int r1 = r0 + 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + dsub;                 // multiple of 4: 8 bytes in one chunk
-        const int ch = col >> 3;
-        const int hf = (col & 7) * 2;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs + r0 * TL::ROWB + ((ch ^ TL::swz_v(r0)) * 16) + hf));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs + r1 * TL::ROWB + ((ch ^ TL::swz_v(r1)) * 16) + hf));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 av4 = {l2.x, l2.y, h2.x, h2.y};
-        o[db] = E::mfma(as_v8<V8>(av4), pb, o[db]);
-      }
-    }
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
   };
 
-  // The visited tiles are split into KS contiguous ranges, one per group of RB waves.
-  // Step i of a range: barrier (tile i, written during step i-1, is visible; the slot
-  // read at step i-1 is free), write tile i+1 from registers into that slot, load tile
-  // i+2 into the registers, compute tile i.  Every wave runs the same number of steps
-  // so the workgroup barriers line up.
+  // The visited tiles are split into KS contiguous ranges, one per group of RB waves;
+  // this wave's rows need the tiles of its range below we.  Every wave runs the same
+  // number of steps so the workgroup barriers line up.
   const int nt = plan.n_visit;
   const int per = (nt + KS - 1) / KS;
-  const int tb = kh * per;
+  const int tb = min(nt, kh * per);
   const int te = min(nt, tb + per);
-  if (tb < te) {
-    load_tile(tb);
-    store_tile(0);
+  const int we = max(tb, min(te, wplan.n_visit));
+  const int nr = te - tb;
+
+  if (nr > 0) {
+    load_k(tb);
+    store_k(0);
+    load_v(tb);
+    store_v(0);
   }
-  if (tb + 1 < te) load_tile(tb + 1);
-  for (int i = 0; i < per; ++i) {
+  if (nr > 1) {
+    load_k(tb + 1);
+    store_k(1);
+    load_v(tb + 1);
+  }
+  if (nr > 2) load_k(tb + 2);
+  __syncthreads();
+  f32x16 sa[KB], sb[KB];
+  if (tb < we) {
+    score_part(sa, 0, 0, KC);
+    bool moved;
+    row_max(sa, tb, moved);   // O is still zero: no rescale needed
+  }
+
+  // One step: tile t = tb + i is in `cur` (scored, its max taken); tile t+1 is scored
+  // into `nxt`.
+  auto step = [&](int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
     const int t = tb + i;
-    __syncthreads();
-    if (t + 1 < te) store_tile((i + 1) & 1);
-    if (t + 2 < te) load_tile(t + 2);
-    if (t < te && t < wplan.n_visit) compute_tile(t, i & 1);
+    __syncthreads();   // writes of the step before are visible; the slots written below are free
+    if (t + 2 < te) store_k(i & 1);
+    if (t + 1 < te) store_v((i + 1) & 1);
+    if (t + 3 < te) load_k(t + 3);
+    if (t + 2 < te) load_v(t + 2);
+
+    const bool has_cur = t < we;
+    const bool has_nxt = t + 1 < we;
+    const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
+    float l0 = 0.f, l1 = 0.f;
+    if (has_cur && has_nxt) {
+      // steady state: one basic block, chunk by chunk
+#pragma unroll
+      for (int cc = 0; cc < PC; ++cc) {
+        score_part(nxt, (i + 1) & 1, cc * KC / PC, (cc + 1) * KC / PC);
+        const u32x4 p = probs_chunk(cur, cc, m_use, l0, l1);
+        pv_chunk(p, i & 1, cc);
+      }
+    } else if (has_cur) {
+#pragma unroll
+      for (int cc = 0; cc < PC; ++cc) pv_chunk(probs_chunk(cur, cc, m_use, l0, l1), i & 1, cc);
+    } else if (has_nxt) {
+      score_part(nxt, (i + 1) & 1, 0, KC);
+    }
+    l_i += l0 + l1;
+    if (has_nxt) {
+      bool moved;
+      const float alpha = row_max(nxt, t + 1, moved);
+      if (moved) rescale_o(alpha);
+    }
+  };
+  for (int i = 0; i < per; i += 2) {
+    step(i, sa, sb);
+    if (i + 1 < per) step(i + 1, sb, sa);
   }
 
   if constexpr (KS == 2) {
