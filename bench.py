@@ -51,24 +51,28 @@ def _log(*a):
 
 
 def _time_launches(fn, steps, warmup, torch):
-    """Per-launch HIP-event durations (ms) plus the whole-region time (ms)."""
+    """Average launch duration (ms) over back-to-back launches between HIP events.
+
+    The timed region holds only the launches (no event between two launches), so the
+    host-side launch cost overlaps the previous kernel and the average is the device
+    time per launch.  It is split into up to five equal blocks, each bracketed by its
+    own events, for the spread.  Returns (block averages, region time)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
+    nblk = max(1, min(5, steps))
+    sizes = [steps // nblk + (1 if i < steps % nblk else 0) for i in range(nblk)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
     torch.cuda.synchronize()
-    region0.record(stream)
-    for a, b in evs:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    region1.record(stream)
+    evs[0].record(stream)
+    for i, n in enumerate(sizes):
+        for _ in range(n):
+            fn()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in evs]
-    return per, region0.elapsed_time(region1)
+    per = [evs[i].elapsed_time(evs[i + 1]) / n for i, n in enumerate(sizes)]
+    return per, evs[0].elapsed_time(evs[-1])
 
 
 def _fwd_flops(B, Hq, Sq, Sk, d, causal):
@@ -84,7 +88,7 @@ def bench_fwd(name, w, steps, warmup, torch, eta):
     fn = lambda: eta.attn_fwd(q, k, v, scale=p["scale"], causal=p["causal"], o=o, lse=lse)
     per, region = _time_launches(fn, steps, warmup, torch)
     flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
-    med = statistics.median(per)
+    med = region / steps
     return {"workload": name, "kernel": "fwd_kernel", "ms_median": med, "ms_region_per_step": region / steps,
             "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
             "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}, (q, k, v, o, lse)
@@ -103,7 +107,7 @@ def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta):
                               grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv)
     per, region = _time_launches(fn, steps, warmup, torch)
     flops = 2.5 * _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
-    med = statistics.median(per)
+    med = region / steps
     return {"workload": name, "kernel": "bwd (preprocess + main + convert)", "ms_median": med,
             "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
             "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}
@@ -122,7 +126,7 @@ def bench_decode(name, w, steps, warmup, torch, eta):
     per, region = _time_launches(fn, steps, warmup, torch)
     total_keys = int(t["seqlens"].sum())
     kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
-    med = statistics.median(per)
+    med = region / steps
     return {"workload": name, "kernel": "decode split + merge", "ms_median": med,
             "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
             "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
@@ -137,7 +141,7 @@ def bench_fp8(name, w, steps, warmup, torch, eta):
     fn = lambda: eta.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, scale=p["scale"], o=o, lse=lse)
     per, region = _time_launches(fn, steps, warmup, torch)
     flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], False)
-    med = statistics.median(per)
+    med = region / steps
     return {"workload": name, "kernel": "fp8_fwd_kernel", "ms_median": med,
             "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": "fp8_e4m3",
             "peak": PEAK_TFLOPS["fp8"], "frac_of_bf16_peak": flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],

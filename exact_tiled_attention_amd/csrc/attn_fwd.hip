@@ -2,11 +2,15 @@
 //
 // Schedule ("M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary",
 // section 0x03, Algorithm 1, and section 0x05C, split-Q): one workgroup owns one
-// query tile of one (batch, query head); each wave owns 32 disjoint query rows, so no
-// output is merged across waves that share a key range.  The workgroup streams K/V
-// tiles of BC keys through an LDS ring and every wave carries the online state
+// query tile of one (batch, query head); each wave owns QB blocks of 32 disjoint query
+// rows, so no output is merged across waves that share a key range.  The workgroup
+// streams K/V tiles through an LDS ring and every wave carries the online state
 // (m, l, u) of its rows in registers ("M4.3 - IO-Aware Attention ...", section 0x09C;
-// FA2 section 0x02C: u <- alpha u + P~ V, normalised once at the end).
+// FA2 section 0x02C: u <- alpha u + P~ V, normalised once at the end).  With two
+// query blocks per wave (head dimension 64) every K and V fragment read from LDS feeds
+// two matrix-core products, halving the LDS traffic per product; the tiles are then
+// 32 keys long to bound the registers.  Small grids split the key range over KS
+// groups of waves, merged at the end.
 //
 // Orientation.  The kernel computes the transposed score tile S^T = K Q^T on the
 // 32x32x16 matrix core: in the accumulator layout each lane then holds ONE query
@@ -57,13 +61,13 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr float kTau = 8.f;   // conditional-rescale threshold, base-2 units
-constexpr int BC = 64;        // keys per K/V tile
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Tile geometry for head dimension D: rows of D*2 bytes, CPR 16-byte chunks per row.
-template <int D>
+// Tile geometry for head dimension D and BC keys: rows of D*2 bytes, CPR 16-byte
+// chunks per row.
+template <int D, int BC>
 struct Tile {
   static constexpr int ROWB = D * 2;
   static constexpr int CPR = D / 8;
@@ -86,29 +90,34 @@ __device__ inline float max_pair32(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename T, int D, int NW, int KS, bool CAUSAL>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+template <typename T, int D, int QB, int RW, int KS, bool CAUSAL>
+__global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
-  typedef Tile<D> TL;
-  constexpr int RB = NW / KS;                 // 32-row query blocks per workgroup
-  constexpr int BQ = RB * 32;
+  constexpr int BC = QB == 2 ? 32 : 64;       // keys per K/V tile
+  typedef Tile<D, BC> TL;
+  constexpr int BQ = RW * QB * 32;            // query rows per workgroup
   constexpr int KC = D / 16;                  // contraction chunks for S^T
   constexpr int KB = BC / 32;                 // key blocks of 32 per tile
   constexpr int DB = D / 32;                  // output d blocks of 32
   constexpr int PC = BC / 16;                 // key chunks of 16 for P V
+  constexpr int KPC = KC / PC;                // score contraction chunks per key chunk
   constexpr int RING = 4 * TL::BYTES;         // K slots 0, 1 then V slots 0, 1
-  constexpr int NTK = RB * kWave;             // threads staging one key range
+  constexpr int NTK = RW * kWave;             // threads staging one key range
   constexpr int LOADS = TL::CHUNKS / NTK;     // 16-byte K (and V) chunks per thread
-  static_assert(TL::CHUNKS % NTK == 0, "chunks must split evenly over the threads");
+  static_assert(TL::CHUNKS % NTK == 0 && LOADS >= 1, "chunks must split evenly over the threads");
+  static_assert(KC % PC == 0, "score product must split evenly over the key chunks");
+  constexpr int NV = 2 + 16 * DB;             // merged values per lane and query block
+  constexpr int MERGE = RW * QB * NV * kWave * 4;
+  constexpr int LDS = (KS > 1 && MERGE > KS * RING) ? MERGE : KS * RING;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KS * RING];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_all[LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int kh = wave / RB;                   // key range of this wave
-  const int w = wave % RB;                    // query block of this wave
+  const int kh = wave / RW;                   // key range of this wave
+  const int w = wave % RW;                    // query rows of this wave
   const int n = lane & 31;
   const int grp = lane >> 5;
   const int tid = threadIdx.x % NTK;          // index among the threads of this key range
@@ -132,69 +141,70 @@ void fwd_kernel(FwdArgs a) {
 
   const int q0 = qt * BQ;
   const int q1 = min(q0 + BQ, a.Sq);
-  const int qrow = q0 + w * 32 + n;
   const TilePlan plan = plan_rows(q0, q1, a.Sq, a.Sk, BC, CAUSAL);
-  const int w0 = q0 + w * 32;
-  const int w1 = max(min(w0 + 32, a.Sq), w0 + 1);
+  const int w0 = q0 + w * QB * 32;
+  const int w1 = max(min(w0 + QB * 32, a.Sq), w0 + 1);
   const TilePlan wplan = plan_rows(w0, w1, a.Sq, a.Sk, BC, CAUSAL);
-  // keys at or past klim are invisible to this lane's query row
-  const int klim = CAUSAL ? min(a.Sk, qrow + (a.Sk - a.Sq) + 1) : a.Sk;
+  int qrow[QB], klim[QB];   // this lane's query row per block; keys at or past klim are invisible
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    qrow[j] = w0 + 32 * j + n;
+    klim[j] = CAUSAL ? min(a.Sk, qrow[j] + (a.Sk - a.Sq) + 1) : a.Sk;
+  }
 
   // Q^T fragments (B operand): lane column = its query row, slots = d 16kc+8g .. +8.
   // A negative score scale is moved into Q (sign flip) so that c > 0 below and the
   // row max can be taken on the raw accumulator values.
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
-  V8 qf[KC];
+  V8 qf[QB][KC];
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    u32x4 raw = buf_load_16(qr, (uint32_t)(qrow * D + 16 * kc + 8 * grp) * 2);
-    raw.x ^= qsign;
-    raw.y ^= qsign;
-    raw.z ^= qsign;
-    raw.w ^= qsign;
-    qf[kc] = as_v8<V8>(raw);
-  }
+  for (int j = 0; j < QB; ++j)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 raw = buf_load_16(qr, (uint32_t)(qrow[j] * D + 16 * kc + 8 * grp) * 2);
+      raw.x ^= qsign;
+      raw.y ^= qsign;
+      raw.z ^= qsign;
+      raw.w ^= qsign;
+      qf[j][kc] = as_v8<V8>(raw);
+    }
 
-  f32x16 o[DB];
+  f32x16 o[QB][DB];
+  float m_i[QB], l_i[QB];   // running max (base-2 units); this lane's share of l
 #pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x16{};
-  float m_i = -INFINITY;   // running max (base-2 units)
-  float l_i = 0.f;         // this lane's share of the running denominator
+  for (int j = 0; j < QB; ++j) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[j][i] = f32x16{};
+    m_i[j] = -INFINITY;
+    l_i[j] = 0.f;
+  }
 
   // Staging: chunk idx = r * NTK + tid of a tile is LDS (row, pos) = (idx / CPR,
   // idx % CPR) and holds global chunk pos ^ swz(row) of that row.
   u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_k = [&](int t) {
+  auto load_tile = [&](u32x4 (&dst)[LOADS], __amdgpu_buffer_rsrc_t src, int t, bool is_v) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
       const int idx = r * NTK + tid;
       const int row = idx / TL::CPR;
       const int pos = idx % TL::CPR;
-      kreg[r] = buf_load_16(kr, (uint32_t)((t * BC + row) * D) * 2 + (uint32_t)((pos ^ TL::swz_k(row)) * 16));
+      const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
+      dst[r] = buf_load_16(src, (uint32_t)((t * BC + row) * D) * 2 + (uint32_t)((pos ^ sw) * 16));
     }
   };
-  auto load_v = [&](int t) {
+  auto store_tile = [&](const u32x4 (&src)[LOADS], uint8_t* slot_base) {
 #pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int idx = r * NTK + tid;
-      const int row = idx / TL::CPR;
-      const int pos = idx % TL::CPR;
-      vreg[r] = buf_load_16(vr, (uint32_t)((t * BC + row) * D) * 2 + (uint32_t)((pos ^ TL::swz_v(row)) * 16));
-    }
+    for (int r = 0; r < LOADS; ++r) st_lds_16(slot_base + (r * NTK + tid) * 16, src[r]);
   };
-  auto store_k = [&](int slot) {
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) st_lds_16(kring + slot * TL::BYTES + (r * NTK + tid) * 16, kreg[r]);
-  };
-  auto store_v = [&](int slot) {
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) st_lds_16(vring + slot * TL::BYTES + (r * NTK + tid) * 16, vreg[r]);
-  };
+  auto load_k = [&](int t) { load_tile(kreg, kr, t, false); };
+  auto load_v = [&](int t) { load_tile(vreg, vr, t, true); };
+  auto store_k = [&](int slot) { store_tile(kreg, kring + slot * TL::BYTES); };
+  auto store_v = [&](int slot) { store_tile(vreg, vring + slot * TL::BYTES); };
 
-  // S^T MFMAs for contraction chunks [kc0, kc1) of one tile from K slot `slot`; the
-  // chunk kc = 0 starts from a zero accumulator.
-  auto score_part = [&](f32x16 (&sc)[KB], int slot, int kc0, int kc1) {
+  // S^T MFMAs for contraction chunks [kc0, kc1) of one tile from K slot `slot`, each K
+  // fragment shared by the QB query blocks; chunk kc = 0 starts from zero.
+  auto score_part = [&](f32x16 (&sc)[QB][KB], int slot, int kc0, int kc1) {
     const uint8_t* ks = kring + slot * TL::BYTES;
 #pragma unroll
     for (int kc = kc0; kc < kc1; ++kc) {
@@ -203,18 +213,19 @@ void fwd_kernel(FwdArgs a) {
         const int row = kbk * 32 + n;
         const int chunk = (2 * kc + grp) ^ TL::swz_k(row);
         const V8 av = as_v8<V8>(ld_lds_16(ks + row * TL::ROWB + chunk * 16));
-        sc[kbk] = E::mfma(av, qf[kc], kc == 0 ? f32x16{} : sc[kbk]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) sc[j][kbk] = E::mfma(av, qf[j][kc], kc == 0 ? f32x16{} : sc[j][kbk]);
       }
     }
   };
 
-  // O^T += V^T P^T for key chunk cc from V slot `slot`.  The 16-lane group G =
-  // lane/16 reads the 4 keys x 16 d block at keys 16cc + 4g (+8 for slots 4..7),
-  // d = 32db + 16(G%2); lane s of the group addresses key row s/4, d columns
-  // 4(s%4) .. +3.
+  // O^T += V^T P^T for key chunk cc from V slot `slot`, each V^T fragment shared by
+  // the QB query blocks.  The 16-lane group G = lane/16 reads the 4 keys x 16 d block
+  // at keys 16cc + 4g (+8 for slots 4..7), d = 32db + 16(G%2); lane s of the group
+  // addresses key row s/4, d columns 4(s%4) .. +3.
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-  auto pv_chunk = [&](const u32x4& p, int slot, int cc) {
+  auto pv_chunk = [&](const u32x4 (&p)[QB], int slot, int cc) {
     const uint8_t* vs = vring + slot * TL::BYTES;
     const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
     const int r1 = r0 + 8;
@@ -230,13 +241,14 @@ void fwd_kernel(FwdArgs a) {
       const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
       const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
       const u32x4 av4 = {l2.x, l2.y, h2.x, h2.y};
-      o[db] = E::mfma(as_v8<V8>(av4), as_v8<V8>(p), o[db]);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) o[j][db] = E::mfma(as_v8<V8>(av4), as_v8<V8>(p[j]), o[j][db]);
     }
   };
 
-  // Probabilities of key chunk cc of a scored tile, packed to the element type
-  // (slot j of lane group g = key 16cc + 8(j/4) + 4g + j%4, accumulator registers
-  // 8(cc%2) .. +7 of key block cc/2); their fp32 sum goes to l.
+  // Probabilities of key chunk cc of a scored tile for query block j, packed to the
+  // element type (slot s of lane group g = key 16cc + 8(s/4) + 4g + s%4, accumulator
+  // registers 8(cc%2) .. +7 of key block cc/2); their fp32 sum goes to l.
   auto probs_chunk = [&](const f32x16 (&sc)[KB], int cc, float m_use, float& l0, float& l1) -> u32x4 {
     const int kbk = cc >> 1;
     const int hb = (cc & 1) * 8;
@@ -252,46 +264,56 @@ void fwd_kernel(FwdArgs a) {
     return u32x4{pk[0], pk[1], pk[2], pk[3]};
   };
 
-  // Row max of tile t and the rescale decision; l is rescaled here, O by the caller
-  // (after the pending P V product).
-  auto row_max = [&](f32x16 (&sc)[KB], int t, bool& moved) -> float {
-    if (t >= wplan.first_masked) {
+  // Row max of tile t and the rescale decision (one per wave, over its QB blocks); l
+  // is rescaled here, O by the caller (after the pending P V product).
+  auto row_max = [&](f32x16 (&sc)[QB][KB], int t, float (&alpha)[QB]) -> bool {
+    float mx[QB];
+    bool up = false;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      if (t >= wplan.first_masked) {
+#pragma unroll
+        for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
+            sc[j][kbk][i] = key < klim[j] ? sc[j][kbk][i] : -INFINITY;
+          }
+      }
+      float r0 = vmax(sc[j][0][0], sc[j][0][1]), r1 = vmax(sc[j][0][2], sc[j][0][3]);
 #pragma unroll
       for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
-          sc[kbk][i] = key < klim ? sc[kbk][i] : -INFINITY;
+        for (int i = (kbk == 0 ? 4 : 0); i < 16; i += 4) {
+          r0 = vmax(r0, vmax(sc[j][kbk][i], sc[j][kbk][i + 1]));
+          r1 = vmax(r1, vmax(sc[j][kbk][i + 2], sc[j][kbk][i + 3]));
         }
+      mx[j] = max_pair32(vmax(r0, r1) * c);
+      up = up || (mx[j] > m_i[j] + kTau);
     }
-    float r0 = vmax(sc[0][0], sc[0][1]), r1 = vmax(sc[0][2], sc[0][3]);
-#pragma unroll
-    for (int kbk = 0; kbk < KB; ++kbk)
-#pragma unroll
-      for (int i = (kbk == 0 ? 4 : 0); i < 16; i += 4) {
-        r0 = vmax(r0, vmax(sc[kbk][i], sc[kbk][i + 1]));
-        r1 = vmax(r1, vmax(sc[kbk][i + 2], sc[kbk][i + 3]));
-      }
-    const float mx = max_pair32(vmax(r0, r1) * c);
-    moved = wave_any(mx > m_i + kTau);
-    float alpha = 1.f;
+    const bool moved = wave_any(up);
     if (moved) {
-      const float m_new = fmaxf(m_i, mx);
-      // the decision is per wave: a row with nothing visible yet keeps m = -inf, alpha 1
-      alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_i - m_new);
-      m_i = m_new;
-      l_i *= alpha;
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const float m_new = fmaxf(m_i[j], mx[j]);
+        // the decision is per wave: a row with nothing visible yet keeps m = -inf, alpha 1
+        alpha[j] = (m_new == -INFINITY) ? 1.f : fast_exp2(m_i[j] - m_new);
+        m_i[j] = m_new;
+        l_i[j] *= alpha[j];
+      }
     }
-    return alpha;
+    return moved;
   };
-  auto rescale_o = [&](float alpha) {
+  auto rescale_o = [&](const float (&alpha)[QB]) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int j = 0; j < QB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[j][db][r] *= alpha[j];
   };
 
-  // The visited tiles are split into KS contiguous ranges, one per group of RB waves;
+  // The visited tiles are split into KS contiguous ranges, one per group of RW waves;
   // this wave's rows need the tiles of its range below we.  Every wave runs the same
   // number of steps so the workgroup barriers line up.
   const int nt = plan.n_visit;
@@ -301,29 +323,36 @@ void fwd_kernel(FwdArgs a) {
   const int we = max(tb, min(te, wplan.n_visit));
   const int nr = te - tb;
 
-  if (nr > 0) {
-    load_k(tb);
-    store_k(0);
-    load_v(tb);
-    store_v(0);
+  // Prologue: K(tb), V(tb), K(tb+1) into LDS; V(tb+1), K(tb+2) into the staging
+  // registers.  All five loads are issued before the first LDS write waits.
+  {
+    u32x4 k0[LOADS], v0[LOADS], k1[LOADS];
+    if (nr > 0) {
+      load_tile(k0, kr, tb, false);
+      load_tile(v0, vr, tb, true);
+    }
+    if (nr > 1) {
+      load_tile(k1, kr, tb + 1, false);
+      load_v(tb + 1);
+    }
+    if (nr > 2) load_k(tb + 2);
+    if (nr > 0) {
+      store_tile(k0, kring);
+      store_tile(v0, vring);
+    }
+    if (nr > 1) store_tile(k1, kring + TL::BYTES);
   }
-  if (nr > 1) {
-    load_k(tb + 1);
-    store_k(1);
-    load_v(tb + 1);
-  }
-  if (nr > 2) load_k(tb + 2);
   __syncthreads();
-  f32x16 sa[KB], sb[KB];
+  f32x16 sa[QB][KB], sb[QB][KB];
   if (tb < we) {
     score_part(sa, 0, 0, KC);
-    bool moved;
-    row_max(sa, tb, moved);   // O is still zero: no rescale needed
+    float alpha[QB];
+    row_max(sa, tb, alpha);   // O is still zero: no rescale needed
   }
 
   // One step: tile t = tb + i is in `cur` (scored, its max taken); tile t+1 is scored
   // into `nxt`.
-  auto step = [&](int i, f32x16 (&cur)[KB], f32x16 (&nxt)[KB]) {
+  auto step = [&](int i, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
     const int t = tb + i;
     __syncthreads();   // writes of the step before are visible; the slots written below are free
     if (t + 2 < te) store_k(i & 1);
@@ -333,27 +362,41 @@ void fwd_kernel(FwdArgs a) {
 
     const bool has_cur = t < we;
     const bool has_nxt = t + 1 < we;
-    const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
-    float l0 = 0.f, l1 = 0.f;
+    float m_use[QB], l0[QB], l1[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      m_use[j] = (m_i[j] == -INFINITY) ? 0.f : m_i[j];
+      l0[j] = 0.f;
+      l1[j] = 0.f;
+    }
+    auto probs = [&](int cc, u32x4 (&p)[QB]) {
+#pragma unroll
+      for (int j = 0; j < QB; ++j) p[j] = probs_chunk(cur[j], cc, m_use[j], l0[j], l1[j]);
+    };
     if (has_cur && has_nxt) {
       // steady state: one basic block, chunk by chunk
 #pragma unroll
       for (int cc = 0; cc < PC; ++cc) {
-        score_part(nxt, (i + 1) & 1, cc * KC / PC, (cc + 1) * KC / PC);
-        const u32x4 p = probs_chunk(cur, cc, m_use, l0, l1);
+        score_part(nxt, (i + 1) & 1, cc * KPC, (cc + 1) * KPC);
+        u32x4 p[QB];
+        probs(cc, p);
         pv_chunk(p, i & 1, cc);
       }
     } else if (has_cur) {
 #pragma unroll
-      for (int cc = 0; cc < PC; ++cc) pv_chunk(probs_chunk(cur, cc, m_use, l0, l1), i & 1, cc);
+      for (int cc = 0; cc < PC; ++cc) {
+        u32x4 p[QB];
+        probs(cc, p);
+        pv_chunk(p, i & 1, cc);
+      }
     } else if (has_nxt) {
       score_part(nxt, (i + 1) & 1, 0, KC);
     }
-    l_i += l0 + l1;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) l_i[j] += l0[j] + l1[j];
     if (has_nxt) {
-      bool moved;
-      const float alpha = row_max(nxt, t + 1, moved);
-      if (moved) rescale_o(alpha);
+      float alpha[QB];
+      if (row_max(nxt, t + 1, alpha)) rescale_o(alpha);
     }
   };
   for (int i = 0; i < per; i += 2) {
@@ -361,91 +404,104 @@ void fwd_kernel(FwdArgs a) {
     if (i + 1 < per) step(i + 1, sb, sa);
   }
 
-  if constexpr (KS == 2) {
-    // Merge the two key ranges' states of each row in one max frame ("M4.3 -
-    // IO-Aware Attention ...", section 0x08B); the second range hands its (m, l, u)
-    // to the first through LDS.  Layout [block][value][lane] keeps lanes on banks.
-    constexpr int NV = 2 + 16 * DB;
-    static_assert(RB * NV * kWave * 4 <= KS * RING, "merge buffer fits in the ring");
-    __syncthreads();                                   // every wave is done with the ring
+  if constexpr (KS > 1) {
+    // Merge the key ranges' states of each row in one max frame ("M4.3 - IO-Aware
+    // Attention ...", section 0x08B): range r hands its (m, l, u) to range 0 through
+    // LDS, one range per round.  Layout [wave][block][value][lane] keeps lanes on banks.
     float* xf = reinterpret_cast<float*>(lds_all);
-    float* mine = xf + (w * NV) * kWave + lane;
-    if (kh == 1) {
-      mine[0] = m_i;
-      mine[kWave] = l_i;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int r = 1; r < KS; ++r) {
+      __syncthreads();                                 // the ring / previous round is free
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mine[(2 + 16 * db + i) * kWave] = o[db][i];
-    }
-    __syncthreads();
-    if (kh == 0) {
-      const float m1 = mine[0];
-      const float l1 = mine[kWave];
-      const float m = fmaxf(m_i, m1);
-      const float a0 = (m == -INFINITY) ? 0.f : fast_exp2(m_i - m);
-      const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m1 - m);
-      l_i = a0 * l_i + a1 * l1;
+      for (int j = 0; j < QB; ++j) {
+        float* slot = xf + ((w * QB + j) * NV) * kWave + lane;
+        if (kh == r) {
+          slot[0] = m_i[j];
+          slot[kWave] = l_i[j];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] = a0 * o[db][i] + a1 * mine[(2 + 16 * db + i) * kWave];
-      m_i = m;
+            for (int q = 0; q < 16; ++q) slot[(2 + 16 * db + q) * kWave] = o[j][db][q];
+        }
+      }
+      __syncthreads();
+      if (kh == 0) {
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          const float* slot = xf + ((w * QB + j) * NV) * kWave + lane;
+          const float m1 = slot[0];
+          const float l1 = slot[kWave];
+          const float m = fmaxf(m_i[j], m1);
+          const float a0 = (m == -INFINITY) ? 0.f : fast_exp2(m_i[j] - m);
+          const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m1 - m);
+          l_i[j] = a0 * l_i[j] + a1 * l1;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) o[j][db][q] = a0 * o[j][db][q] + a1 * slot[(2 + 16 * db + q) * kWave];
+          m_i[j] = m;
+        }
+      }
     }
   }
 
   // Epilogue: O = u / l once per row; LSE = (m + log2 l) ln 2 (FA2 section 0x02D).
-  const float l_tot = l_i + __shfl_xor(l_i, 32);
-  const bool empty = (m_i == -INFINITY) || !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  if (kh == 0 && qrow < a.Sq) {
-    T* ob = reinterpret_cast<T*>(a.o) + ((int64_t)(b * a.Hq + h) * a.Sq + qrow) * D;
+  if (kh == 0) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int j = 0; j < QB; ++j) {
+      const float l_tot = l_i[j] + __shfl_xor(l_i[j], 32);
+      const bool empty = (m_i[j] == -INFINITY) || !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      if (qrow[j] < a.Sq) {
+        T* ob = reinterpret_cast<T*>(a.o) + ((int64_t)(b * a.Hq + h) * a.Sq + qrow[j]) * D;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 pk;
-        pk.x = E::pack2(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
-        pk.y = E::pack2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(ob + db * 32 + 8 * r4 + 4 * grp) = pk;
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            u32x2 pk;
+            pk.x = E::pack2(o[j][db][4 * r4 + 0] * inv, o[j][db][4 * r4 + 1] * inv);
+            pk.y = E::pack2(o[j][db][4 * r4 + 2] * inv, o[j][db][4 * r4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(ob + db * 32 + 8 * r4 + 4 * grp) = pk;
+          }
+        }
+        if (a.lse != nullptr && grp == 0) {
+          a.lse[(int64_t)(b * a.Hq + h) * a.Sq + qrow[j]] = empty ? -INFINITY : (m_i[j] + __log2f(l_tot)) * ATTN_LN2;
+        }
       }
-    }
-    if (a.lse != nullptr && grp == 0) {
-      a.lse[(int64_t)(b * a.Hq + h) * a.Sq + qrow] = empty ? -INFINITY : (m_i + __log2f(l_tot)) * ATTN_LN2;
     }
   }
 }
 
-template <typename T, int D, int NW, int KS>
+template <typename T, int D, int QB, int RW, int KS>
 hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   FwdArgs a = a0;
-  constexpr int BQ = (NW / KS) * 32;
+  constexpr int BQ = RW * QB * 32;
   a.nqt = (a.Sq + BQ - 1) / BQ;
   const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
-  const dim3 block(NW * kWave);
+  const dim3 block(RW * KS * kWave);
   if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, NW, KS, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, D, NW, KS, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-// Eight waves per workgroup.  When 256-row query tiles would leave fewer than two
-// workgroups per compute unit, the waves split into two groups that stream the two
-// halves of the K/V range for 128-row tiles instead (merged at the end).
+// Eight waves per workgroup.  Head dimension 64: two query blocks per wave, 4 row
+// waves x 2 key ranges (256 rows) when that gives every compute unit a workgroup,
+// else 2 row waves x 4 key ranges (128 rows).  Head dimension 128 (register bound):
+// one query block per wave, 8 row waves (256 rows), or 4 x 2 key ranges (128 rows)
+// for grids under two workgroups per compute unit.
 constexpr int kCUs = 256;
-
-template <typename T, int D>
-hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  const int64_t wgs_full = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
-  if (wgs_full >= 2 * kCUs) return launch_fwd_t<T, D, 8, 1>(a, stream);
-  return launch_fwd_t<T, D, 8, 2>(a, stream);
-}
 
 template <typename T>
 hipError_t launch_fwd_dtype(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return launch_fwd_d<T, 64>(a, stream);
-  return launch_fwd_d<T, 128>(a, stream);
+  const int64_t wgs256 = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
+  if (a.d == 64) {
+    if (wgs256 >= kCUs) return launch_fwd_t<T, 64, 2, 4, 2>(a, stream);
+    return launch_fwd_t<T, 64, 2, 2, 4>(a, stream);
+  }
+  if (wgs256 >= 2 * kCUs) return launch_fwd_t<T, 128, 1, 8, 1>(a, stream);
+  return launch_fwd_t<T, 128, 1, 4, 2>(a, stream);
 }
 
 }  // namespace

@@ -84,6 +84,18 @@ def test_fwd_config3_full_size_sampled():
     _check(w, rows=rows, heads=heads)
 
 
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (64, "bf16"), (128, "bf16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_large_grid_sampled(d, dtype, causal):
+    """Grids of at least one 256-row workgroup per compute unit (the single-key-range
+    and two-key-range launch shapes), with query and key tails."""
+    need_gpu()
+    w = attn_inputs.prefill(2, 64, 16, 1100, 1070, d, dtype, seed=31 + d, causal=causal)
+    rows = np.unique(np.concatenate([np.arange(0, 1100, 37), [0, 255, 256, 1023, 1024, 1099]]))
+    heads = [(0, 0), (0, 63), (1, 17), (1, 40)]
+    _check(w, rows=rows, heads=heads)
+
+
 def test_fwd_bitwise_repeatable():
     need_gpu()
     import exact_tiled_attention_amd as eta
