@@ -7,17 +7,22 @@
 // "M4.3 - IO-Aware Attention ...", sections 0x08B-0x08F: partial (m, l, u) states of
 // disjoint key sets merge exactly, in any order, once they share one max frame).
 //
-// Pass 1 (split): one workgroup per (chunk, batch item, K/V head, head pass).  The
-// chunk is read from HBM exactly once for the G query heads of the pass.  The work is
-// a handful of dot products per key, far too thin for the matrix cores, and the
-// kernel is bound by HBM bandwidth, so it stays on the vector ALUs:
-//   * lane (row group rg, column chunk c8) loads 16 contiguous bytes of a key row, so
-//     every wave-wide load covers whole rows (LPR lanes per row, RPI rows per load);
-//   * q.k partial dots use v_dot2 on packed 16-bit pairs, then a DPP butterfly
-//     (quad_perm, half-mirror, mirror) sums the LPR lanes of a row;
-//   * p.V runs as v_dot2 over pairs of keys after an in-register interleave of V;
-//   * each wave keeps (m, l, u) for its keys; the four waves merge through LDS and
-//     write one partial per (chunk, query head).
+// Pass 1 (split): one workgroup per (chunk, batch item, K/V head, head pass); the
+// chunk is read from HBM exactly once for the G <= 16 query heads of the pass.  Each
+// wave takes 64 keys of the chunk per pass and runs both products on the 16x16x32
+// matrix core, with the G query heads as the N dimension (only G of its 16 columns
+// carry data; the matrix core has the headroom, and the products stay off the vector
+// ALUs, which keeps the kernel bound by HBM):
+//   * every HBM load is a wave-wide 1 KiB of whole K or V rows with the streaming
+//     (non-temporal) hint, the pattern that reads fastest; K and V then pass through
+//     the wave's own LDS region (no workgroup barrier), K first;
+//   * scores S^T = K Q^T: the K fragments (16 keys x 32 d) are read from LDS as the
+//     A operand;
+//   * the accumulator layout puts one head per lane column and 4 keys per lane, so
+//     the probabilities become the A operand of O = P V without moving;
+//   * V is read back transposed with ds_read_b64_tr_b16 as the B operand.
+// The four waves then merge their (m, l, u) through LDS and write one partial per
+// (chunk, query head).
 // Pass 2 (merge): one wave per (batch item, query head) folds the partials in one
 // max frame, O = u / l, LSE = m + ln l (all in base 2 internally).
 #include "attn_device.h"
@@ -26,56 +31,45 @@
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef ATTN_DECODE_SUB
-#define ATTN_DECODE_SUB 64
-#endif
-constexpr int kSub = ATTN_DECODE_SUB;   // keys per wave per sub-tile
+constexpr int kSub = 64;   // keys per wave per pass
 
-template <typename T> struct Dot2;
-template <> struct Dot2<f16> {
-  static __device__ inline float dot(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<f16> {
+  static __device__ inline f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 };
-template <> struct Dot2<bf16> {
-  static __device__ inline float dot(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+template <> struct Mfma16<bf16> {
+  static __device__ inline f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
 
-template <int CTRL> __device__ inline float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
+// 16x16x32 layouts (wave64): A lane l = row l%16, contraction slots from group l/16;
+// B lane l = column l%16, same slots; C lane l = column l%16, rows 4(l/16) .. +3.
 
-// Sum over the LPR consecutive lanes of a row group (LPR = 8 or 16); every lane of the
-// group receives the total.
-template <int LPR> __device__ inline float row_group_sum(float x) {
-  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x);   // row_half_mirror: pairs the two quads of each 8 lanes
-  if (LPR == 16) x += dpp_mov<0x140>(x);   // row_mirror: pairs the two halves of 16
-  return x;
-}
-
-// Combine across row groups (lanes LPR, 2 LPR, ... apart).
-template <int LPR> __device__ inline float across_groups_max(float x) {
-#pragma unroll
-  for (int s = LPR; s < 64; s <<= 1) x = fmaxf(x, __shfl_xor(x, s));
-  return x;
-}
-template <int LPR> __device__ inline float across_groups_sum(float x) {
-#pragma unroll
-  for (int s = LPR; s < 64; s <<= 1) x += __shfl_xor(x, s);
-  return x;
-}
+// K and V rows pass through the wave's LDS region with their 16-byte chunks
+// XOR-swizzled (chunk p of row r at position p ^ swz(r)):
+//  * K: the A-fragment read takes one chunk of 16 consecutive rows per 16-lane group;
+//  * V: one 32-lane pass of the transpose read takes 8 rows x 2 chunks;
+// both swizzles put those accesses on distinct banks.
+template <int D> __device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __device__ inline int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  constexpr int LPR = D / 8;          // lanes per key row (16 bytes each)
-  constexpr int RPI = 64 / LPR;       // key rows per wave-wide load
-  constexpr int NI = kSub / RPI;      // rows per lane per sub-tile
-  typedef Dot2<T> DT;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
+  constexpr int DC = D / 32;          // contraction chunks of the score product
+  constexpr int DB = D / 16;          // 16-wide d blocks of the output
+  constexpr int KT = kSub / 16;       // 16-key score tiles per pass
+  constexpr int CPR = D / 8;          // 16-byte chunks per V row
+  constexpr int VLD = kSub * CPR / 64;   // V chunks staged per lane per pass
+  static_assert(G >= 1 && G <= 16, "heads per pass");
+  typedef Mfma16<T> MF;
 
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[4][kSub * D * 2];
   __shared__ float s_m[4][G];
   __shared__ float s_l[4][G];
   __shared__ float s_u[4][G][D];
@@ -95,100 +89,151 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int rg = lane / LPR;
-  const int c8 = lane % LPR;
+  const int n = lane & 15;
+  const int g = lane >> 4;
 
-  const T* __restrict__ kbase = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Smax) * D;
-  const T* __restrict__ vbase = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Smax) * D;
-  const T* __restrict__ qbase = reinterpret_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h0) * D;
+  const T* kbase = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Smax) * D;
+  const T* vbase = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Smax) * D;
+  // loads past the sequence's length return zero (the buffer range check)
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)len * D * 2);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)len * D * 2);
+  const T* qbase = reinterpret_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h0) * D;
+  uint8_t* vt = s_v[w];
 
-  u32x4 qv[G];
+  // Q^T as the B operand: column n = head h0 + n (zero for n >= G), slots d 32dc + 8g.
+  u32x4 qf[DC];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) qv[hh] = ld_global_16(qbase + (int64_t)hh * D + 8 * c8);
-
-  float m[G], l[G], u[G][8];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) u[hh][j] = 0.f;
+  for (int dc = 0; dc < DC; ++dc) {
+    qf[dc] = u32x4{0u, 0u, 0u, 0u};
+    if (n < G) qf[dc] = ld_global_16(qbase + (int64_t)n * D + 32 * dc + 8 * g);
   }
+
+  // Running state: m (base 2) per head column n (equal on the four lane groups), the
+  // lane's share of l, and the output rows 4g .. 4g+3 (heads) at d = 16db + n.
+  float m_i = -INFINITY, l_i = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int base = kbeg + kSub * w; base < kend; base += 4 * kSub) {
-    u32x4 kr[NI], vr[NI];
+    // All of the pass's loads first, each wave-wide load 1 KiB of whole rows with the
+    // streaming hint (every byte is read once); K then V go through the wave's LDS
+    // region, K first.
+    u32x4 kv[VLD], vv[VLD];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int key = base + rg + RPI * i;
-      u32x4 zk = {0u, 0u, 0u, 0u};
-      u32x4 zv = {0u, 0u, 0u, 0u};
-      if (key < kend) {
-        zk = ld_global_16(kbase + (int64_t)key * D + 8 * c8);
-        zv = ld_global_16(vbase + (int64_t)key * D + 8 * c8);
-      }
-      kr[i] = zk;
-      vr[i] = zv;
-    }
-    // Interleave V by key pairs: vp[i/2][2*dw+e] packs (V[i][d], V[i+1][d]).
-    uint32_t vp[NI / 2][8];
-#pragma unroll
-    for (int i = 0; i < NI; i += 2) {
-#pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        vp[i / 2][2 * dw] = pack_lo(vr[i][dw], vr[i + 1][dw]);
-        vp[i / 2][2 * dw + 1] = pack_hi(vr[i][dw], vr[i + 1][dw]);
-      }
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      kv[r] = buf_load_16_stream(kr, (uint32_t)((base + idx / CPR) * D + 8 * (idx % CPR)) * 2);
     }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float s[NI];
-      float mx = -INFINITY;
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      vv[r] = buf_load_16_stream(vr, (uint32_t)((base + idx / CPR) * D + 8 * (idx % CPR)) * 2);
+    }
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float acc = 0.f;
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      const int row = idx / CPR;
+      st_lds_16(vt + row * D * 2 + (((idx % CPR) ^ swz_k<D>(row)) * 16), kv[r]);
+    }
+    // K fragment (tile kt, contraction chunk dc): row 16kt + n, chunk 4dc + g.
+    u32x4 kf[KT][DC];
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw) acc = DT::dot(qv[hh][dw], kr[i][dw], acc);
-        acc = row_group_sum<LPR>(acc);
-        const int key = base + rg + RPI * i;
-        const float x = key < kend ? acc * a.scale_log2 : -INFINITY;
-        s[i] = x;
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const int row = 16 * kt + n;
+        kf[kt][dc] = ld_lds_16(vt + row * D * 2 + (((4 * dc + g) ^ swz_k<D>(row)) * 16));
+      }
+#pragma unroll
+    for (int r = 0; r < VLD; ++r) {
+      const int idx = r * 64 + lane;
+      const int row = idx / CPR;
+      st_lds_16(vt + row * D * 2 + (((idx % CPR) ^ swz_v<D>(row)) * 16), vv[r]);
+    }
+
+    // Scores: tile kt, lane (g, n) holds keys base + 16kt + 4g + i for head n.
+    f32x4 sc[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      sc[kt] = MF::run(kf[kt][0], qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int dc = 1; dc < DC; ++dc) sc[kt] = MF::run(kf[kt][dc], qf[dc], sc[kt]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = base + 16 * kt + 4 * g + i;
+        const float x = key < kend ? sc[kt][i] * a.scale_log2 : -INFINITY;
+        sc[kt][i] = x;
         mx = fmaxf(mx, x);
       }
-      mx = across_groups_max<LPR>(mx);
-      const float m_new = fmaxf(m[hh], mx);          // finite: key `base` is valid
-      const float alpha = fast_exp2(m[hh] - m_new);
-      float rs = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_i, mx);              // finite: key `base` is valid
+    const float alpha = fast_exp2(m_i - m_new);
+    m_i = m_new;
+    // P as the A operand of O = P V: row n = head, slots 0..3 = keys 32j + 4g + i,
+    // slots 4..7 = keys 32j + 16 + 4g + i.
+    u32x4 pa[KT / 2];
+    float rs = 0.f;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        s[i] = fast_exp2(s[i] - m_new);
-        rs += s[i];
+    for (int j = 0; j < KT / 2; ++j) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = fast_exp2(sc[2 * j][i] - m_new);
+        e[4 + i] = fast_exp2(sc[2 * j + 1][i] - m_new);
       }
-      l[hh] = alpha * l[hh] + rs;
-      m[hh] = m_new;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) u[hh][j] *= alpha;
+      for (int i = 0; i < 8; ++i) rs += e[i];
+      pa[j] = u32x4{Elem<T>::pack2(e[0], e[1]), Elem<T>::pack2(e[2], e[3]), Elem<T>::pack2(e[4], e[5]),
+                    Elem<T>::pack2(e[6], e[7])};
+    }
+    l_i = alpha * l_i + rs;
+    // Output rows are heads 4g + i; their alpha lives in the lanes of column 4g + i.
 #pragma unroll
-      for (int i = 0; i < NI; i += 2) {
-        const uint32_t pp = Elem<T>::pack2(s[i], s[i + 1]);
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) u[hh][j] = DT::dot(pp, vp[i / 2][j], u[hh][j]);
+      for (int db = 0; db < DB; ++db) o[db][i] *= ai;
+    }
+    // V^T fragments by transpose reads: the 16-lane group g reads the 4 keys x 16 d
+    // block at keys 32j + 4g (+16 for slots 4..7), d = 16db; lane s of the group
+    // addresses key row s/4, d columns 4(s%4) .. +3.
+#pragma unroll
+    for (int j = 0; j < KT / 2; ++j) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = 16 * db + 4 * (n & 3);
+        const int r0 = 32 * j + 4 * g + (n >> 2);
+        const int r1 = r0 + 16;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + r0 * D * 2 + (((col >> 3) ^ swz_v<D>(r0)) * 16) + (col & 7) * 2));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vt + r1 * D * 2 + (((col >> 3) ^ swz_v<D>(r1)) * 16) + (col & 7) * 2));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        o[db] = MF::run(pa[j], u32x4{l2.x, l2.y, h2.x, h2.y}, o[db]);
       }
     }
   }
 
-  // Sum each wave's per-lane shares over its row groups, then merge the four waves.
+  // l: sum the four lane groups' shares.  Then merge the four waves through LDS.
+  const float lt = l_i + __shfl_xor(l_i, 16);
+  const float l_tot = lt + __shfl_xor(lt, 32);
+  if (g == 0 && n < G) {
+    s_m[w][n] = m_i;
+    s_l[w][n] = l_tot;
+  }
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float lt = across_groups_sum<LPR>(l[hh]);
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * g + i;
+    if (hh < G) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[hh][j] = across_groups_sum<LPR>(u[hh][j]);
-    if (lane == 0) {
-      s_m[w][hh] = m[hh];
-      s_l[w][hh] = lt;
-    }
-    if (rg == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s_u[w][hh][8 * c8 + j] = u[hh][j];
+      for (int db = 0; db < DB; ++db) s_u[w][hh][16 * db + n] = o[db][i];
     }
   }
   __syncthreads();
@@ -279,8 +324,11 @@ hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Heads per pass: the largest of 16, 8, 4, 2, 1 that divides the group.
 template <typename T, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  if (a.group % 16 == 0) return launch_g<T, D, 16>(a, stream);
+  if (a.group % 8 == 0) return launch_g<T, D, 8>(a, stream);
   if (a.group % 4 == 0) return launch_g<T, D, 4>(a, stream);
   if (a.group % 2 == 0) return launch_g<T, D, 2>(a, stream);
   return launch_g<T, D, 1>(a, stream);
