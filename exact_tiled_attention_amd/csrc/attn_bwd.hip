@@ -18,9 +18,15 @@
 // matrix core with the query rows as M and the wave's keys as N, so each lane holds
 // ONE key and 16 query rows of it: exactly the A-operand shape that dV += P^T dO and
 // dK += dS^T Q need, with no data movement.  Their B operands (dO and Q with the
-// query index as the contraction) come from transposed LDS copies made while the
-// query tile is staged.  dQ needs dS with queries as rows, so dS goes through LDS
-// once; each wave then forms one 32-wide d block of dS K over all 128 keys.
+// query index as the contraction) come from the row-major staged tiles through
+// ds_read_b64_tr_b16 (one column of 4 consecutive rows per lane).  dQ needs dS with
+// queries as rows: dS goes to LDS key-major (8-byte writes of 4 queries) and comes
+// back through the same transpose read; each wave then forms one (query block, d
+// block) of dS K over all 128 keys.  Staged rows are unpadded, their 16-byte chunks
+// XOR-swizzled so that both the 16-byte fragment reads and the transpose reads of a
+// tile hit distinct banks.
+#include <type_traits>
+
 #include "../../include/attn.h"
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -111,20 +117,33 @@ __device__ inline void split_pack8(const f32x16& x, int off, u32x4& hi, u32x4& l
 
 // ---------------------------------------------------------------------------------
 // 2. main column-owner kernel
+//
+// Chunk swizzle of the staged Q / dO rows (chunk p of row r at p ^ swz(r)):
+//  * 16-byte fragment reads: 16 consecutive rows, one chunk -> 16 distinct banks groups;
+//  * transpose reads: 4 consecutive rows x 4 consecutive chunks -> 16 distinct groups.
+template <int D> __device__ inline int swz_q(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  const int k = (r >> 1) & 7;   // rows of 128 bytes: pairs of rows share a 256-byte bank span
+  return (k >> 1) | ((k & 1) << 2);
+}
+
 template <int D, int BQ>
 struct BwdLds {
-  static constexpr int RSTR = D + 8;        // row-major Q / dO stride
-  static constexpr int TSTR = BQ + 4;       // transposed Q^T / dO^T stride
-  static constexpr int SSTR = kBKV + 8;     // dS [q][key] stride
-  static constexpr int KSTR = kBKV + 8;     // K^T [d][key] stride
-  static constexpr int Q = 0;
-  static constexpr int QT = Q + BQ * RSTR;
-  static constexpr int DO = QT + D * TSTR;
-  static constexpr int DOT = DO + BQ * RSTR;
-  static constexpr int DS = DOT + D * TSTR;
-  static constexpr int KT = DS + BQ * SSTR;
-  static constexpr int ELEMS = KT + D * KSTR;   // 16-bit elements
+  static constexpr int ROWB = D * 2;          // staged row bytes
+  static constexpr int Q = 0;                 // byte offsets
+  static constexpr int DO = Q + BQ * ROWB;
+  static constexpr int DST = DO + BQ * ROWB;  // dS^T [key][query], 16-bit
+  static constexpr int KSTR = kBKV + 8;       // K^T [d][key] stride (elements)
+  static constexpr int KT = DST + kBKV * BQ * 2;
+  static constexpr int BYTES = KT + D * KSTR * 2;
 };
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ inline u32x2 tr_read(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
 
 template <typename T, typename G, int D, bool CAUSAL>
 __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
@@ -135,11 +154,12 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
   constexpr int KC = D / 16;                // contraction chunks over d
   constexpr int QC = BQ / 16;               // contraction chunks over queries
   constexpr int DB = D / 32;                // d blocks of 32
+  constexpr int CPR = D / 8;                // 16-byte chunks per staged row
+  constexpr int SCH = BQ * CPR / (kNT / 2); // chunks per staging thread (Q or dO)
   typedef BwdLds<D, BQ> L;
-  constexpr int STAGE_BLOCKS = 2 * (BQ / 4) * (D / 8);   // Q and dO, 4-row x 8-col
-  static_assert(STAGE_BLOCKS == kNT, "one staging block per thread");
+  static_assert(SCH * (kNT / 2) == BQ * CPR, "staging chunks split evenly");
 
-  __shared__ __attribute__((aligned(16))) T lds[L::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
   __shared__ __attribute__((aligned(16))) float s_lse[BQ];
   __shared__ __attribute__((aligned(16))) float s_del[BQ];
 
@@ -148,6 +168,8 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
   const int w = tid >> 6;
   const int n = lane & 31;
   const int grp = lane >> 5;
+  const int s16 = lane & 15;
+  const int hsel = (lane >> 4) & 1;          // 16-lane group within the 32-lane half
 
   const int jt = blockIdx.x;                 // key tile
   const int bkv = blockIdx.y;
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
   }
   // K^T of the whole tile into LDS ([d][key]) for the dQ product: 4-key x 8-d blocks.
   {
-    T* kt = lds + L::KT;
+    T* kt = reinterpret_cast<T*>(lds + L::KT);
     for (int blk = tid; blk < (kBKV / 4) * (D / 8); blk += kNT) {
       const int kq = blk / (D / 8);
       const int dc = blk % (D / 8);
@@ -211,12 +233,11 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
   const int nq = cp.n_qtiles - cp.first_qtile;
   const int nsteps = nq * a.group;
 
-  // staging block of this thread: 4 rows x 8 columns of Q (first half) or dO
-  const int sblk = tid % (kNT / 2);
+  // Staging: the first half of the threads stages Q, the second dO; chunk idx =
+  // r * 128 + (tid % 128) of the tile is (row idx / CPR, chunk idx % CPR).
   const bool stage_do = tid >= kNT / 2;
-  const int srq = sblk / (D / 8);            // row quad
-  const int sdc = sblk % (D / 8);            // column chunk
-  u32x4 sreg[4];
+  const int st_t = tid % (kNT / 2);
+  u32x4 sreg[SCH];
   float slse = 0.f, sdel = 0.f;
 
   auto step_coords = [&](int step, int& h, int& qt) {
@@ -227,11 +248,11 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     int h, qt;
     step_coords(step, h, qt);
     const T* src = reinterpret_cast<const T*>(stage_do ? a.dO : a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * 2);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int qr = qt * BQ + 4 * srq + s;
-      sreg[s] = u32x4{0u, 0u, 0u, 0u};
-      if (qr < a.Sq) sreg[s] = ld_global_16(src + (int64_t)qr * D + sdc * 8);
+    for (int r = 0; r < SCH; ++r) {
+      const int idx = r * (kNT / 2) + st_t;
+      sreg[r] = buf_load_16(rs, (uint32_t)((qt * BQ + idx / CPR) * D + 8 * (idx % CPR)) * 2);
     }
     if (tid < BQ) {
       const int qr = qt * BQ + tid;
@@ -241,19 +262,12 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     }
   };
   auto store_stage = [&]() {
-    T* rm = lds + (stage_do ? L::DO : L::Q);
-    T* tr = lds + (stage_do ? L::DOT : L::QT);
+    uint8_t* dst = lds + (stage_do ? L::DO : L::Q);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) st_lds_16(rm + (4 * srq + s) * L::RSTR + sdc * 8, sreg[s]);
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      u32x2 ev, od;
-      ev.x = pack_lo(sreg[0][wd], sreg[1][wd]);
-      ev.y = pack_lo(sreg[2][wd], sreg[3][wd]);
-      od.x = pack_hi(sreg[0][wd], sreg[1][wd]);
-      od.y = pack_hi(sreg[2][wd], sreg[3][wd]);
-      st_lds_8(tr + (sdc * 8 + 2 * wd) * L::TSTR + 4 * srq, ev);
-      st_lds_8(tr + (sdc * 8 + 2 * wd + 1) * L::TSTR + 4 * srq, od);
+    for (int r = 0; r < SCH; ++r) {
+      const int idx = r * (kNT / 2) + st_t;
+      const int row = idx / CPR;
+      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_q<D>(row)) * 16), sreg[r]);
     }
     if (tid < BQ) {
       s_lse[tid] = slse;
@@ -261,32 +275,26 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     }
   };
 
-  if (nsteps > 0) prefetch(0);
-  for (int step = 0; step < nsteps; ++step) {
-    int h, qt;
-    step_coords(step, h, qt);
-    store_stage();
-    __syncthreads();                                          // (A) stage visible
-    if (step + 1 < nsteps) prefetch(step + 1);
-
-    const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * BQ > a.Sq;
-    const T* sq = lds + L::Q;
-    const T* sdo = lds + L::DO;
-    // S = Q K^T and dP = dO V^T for this wave's 32 keys: lane = key, regs = queries.
+  // One step: S / dP for the wave's keys, P and dS, the dV / dK products, dS^T to LDS.
+  // MASKED applies the element mask (tails and the causal band).
+  auto compute = [&](auto masked_tag, int qt) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const uint8_t* sq = lds + L::Q;
+    const uint8_t* sdo = lds + L::DO;
     f32x16 s[MB], dp[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      s[mb] = f32x16{};
-      dp[mb] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const V8 aq = as_v8<V8>(ld_lds_16(sq + (32 * mb + n) * L::RSTR + 16 * kc + 8 * grp));
-        const V8 ad = as_v8<V8>(ld_lds_16(sdo + (32 * mb + n) * L::RSTR + 16 * kc + 8 * grp));
-        s[mb] = E::mfma(aq, kf[kc], s[mb]);
-        dp[mb] = E::mfma(ad, vf[kc], dp[mb]);
+        const int row = 32 * mb + n;
+        const int off = row * L::ROWB + (((2 * kc + grp) ^ swz_q<D>(row)) * 16);
+        const V8 aq = as_v8<V8>(ld_lds_16(sq + off));
+        const V8 ad = as_v8<V8>(ld_lds_16(sdo + off));
+        s[mb] = E::mfma(aq, kf[kc], kc == 0 ? f32x16{} : s[mb]);
+        dp[mb] = E::mfma(ad, vf[kc], kc == 0 ? f32x16{} : dp[mb]);
       }
     }
-    // P = exp2(S log2e scale - LSE log2e); dS = P (dP - D), both masked before use.
+    // P = exp2(S log2e scale - LSE log2e); dS = P (dP - D).
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -297,8 +305,8 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r4 + e;
-          float pv = fast_exp2(s[mb][i] * a.scale_log2 - lv[e]);
-          if (masked) {
+          float pv = fast_exp2(fmaf(s[mb][i], a.scale_log2, -lv[e]));
+          if constexpr (MASKED) {
             const int qr = qt * BQ + qb + e;
             const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
             pv = vis ? pv : 0.f;
@@ -309,11 +317,11 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
       }
     }
     // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries
-    // 16c + 8(j/4) + 4g + j%4 (registers 8(c%2) + j of query block c/2).
+    // 16c + 8(j/4) + 4g + j%4 (registers 8(c%2) + j of query block c/2); B by
+    // transpose reads of the staged tiles: the 16-lane group reads 4 queries x 16 d
+    // (rows 16c + 4g, +8 for slots 4..7), lane s addressing row s/4, d 4(s%4).
     // With bf16 elements P and dS enter as hi + lo pairs of bf16 values (x = hi + lo
     // to about 16 significant bits), so these two sums keep float32-like precision.
-    const T* sqt = lds + L::QT;
-    const T* sdot = lds + L::DOT;
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
       const int mb = c >> 1;
@@ -321,52 +329,75 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
       u32x4 pp, ss, pl, sl;
       split_pack8<T>(s[mb], hb, pp, pl);
       split_pack8<T>(dp[mb], hb, ss, sl);
-      const V8 pa = as_v8<V8>(pp);
-      const V8 sa = as_v8<V8>(ss);
+      const int r0 = 16 * c + 4 * grp + (s16 >> 2);
+      const int r1 = r0 + 8;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int drow = db * 32 + n;
-        const T* o1 = sdot + drow * L::TSTR + 16 * c + 4 * grp;
-        const T* q1 = sqt + drow * L::TSTR + 16 * c + 4 * grp;
-        const u32x2 olo = ld_lds_8(o1), ohi = ld_lds_8(o1 + 8);
-        const u32x2 qlo = ld_lds_8(q1), qhi = ld_lds_8(q1 + 8);
-        const u32x4 ob = {olo.x, olo.y, ohi.x, ohi.y};
-        const u32x4 qb4 = {qlo.x, qlo.y, qhi.x, qhi.y};
-        dv[db] = E::mfma(pa, as_v8<V8>(ob), dv[db]);
-        dk[db] = E::mfma(sa, as_v8<V8>(qb4), dk[db]);
+        const int col = 32 * db + 16 * hsel + 4 * (s16 & 3);
+        const int o0 = r0 * L::ROWB + (((col >> 3) ^ swz_q<D>(r0)) * 16) + (col & 7) * 2;
+        const int o1 = r1 * L::ROWB + (((col >> 3) ^ swz_q<D>(r1)) * 16) + (col & 7) * 2;
+        const u32x2 olo = tr_read(sdo + o0), ohi = tr_read(sdo + o1);
+        const u32x2 qlo = tr_read(sq + o0), qhi = tr_read(sq + o1);
+        const V8 ob = as_v8<V8>(u32x4{olo.x, olo.y, ohi.x, ohi.y});
+        const V8 qb4 = as_v8<V8>(u32x4{qlo.x, qlo.y, qhi.x, qhi.y});
+        dv[db] = E::mfma(as_v8<V8>(pp), ob, dv[db]);
+        dk[db] = E::mfma(as_v8<V8>(ss), qb4, dk[db]);
         if (kSplit<T>) {
-          dv[db] = E::mfma(as_v8<V8>(pl), as_v8<V8>(ob), dv[db]);
-          dk[db] = E::mfma(as_v8<V8>(sl), as_v8<V8>(qb4), dk[db]);
+          dv[db] = E::mfma(as_v8<V8>(pl), ob, dv[db]);
+          dk[db] = E::mfma(as_v8<V8>(sl), qb4, dk[db]);
         }
       }
     }
-    // dS -> LDS as [query][key] (16-bit) for the dQ product.
-    {
-      T* sds = lds + L::DS;
-      const int kcol = 32 * w + n;
+    // dS^T -> LDS [key][query]: registers 4r4 .. 4r4+3 are 4 consecutive queries.
+    uint8_t* dst = lds + L::DST;
+    const int krow = 32 * w + n;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qloc = 32 * mb + 8 * (i >> 2) + 4 * grp + (i & 3);
-          sds[qloc * L::SSTR + kcol] = E::from_f(dp[mb][i]);
-        }
-    }
-    __syncthreads();                                          // (B) dS visible
-    // dQ_acc += dS K: wave w takes query block qb and d block db; contraction over the
-    // 128 keys, slots = keys 16kc + 8g + j; result lane = d column, regs = queries.
+      for (int r4 = 0; r4 < 4; ++r4) {
+        u32x2 pk;
+        pk.x = E::pack2(dp[mb][4 * r4 + 0], dp[mb][4 * r4 + 1]);
+        pk.y = E::pack2(dp[mb][4 * r4 + 2], dp[mb][4 * r4 + 3]);
+        st_lds_8(dst + (krow * BQ + 32 * mb + 8 * r4 + 4 * grp) * 2, pk);
+      }
+  };
+
+  if (nsteps > 0) prefetch(0);
+  for (int step = 0; step < nsteps; ++step) {
+    int h, qt;
+    step_coords(step, h, qt);
+    // The previous step's reads of the staged tiles ended before its barrier (B), and
+    // this step's dS^T writes come after barrier (A): one barrier pair per step.
+    store_stage();
+    __syncthreads();                                          // (A) stage visible
+    if (step + 1 < nsteps) prefetch(step + 1);
+
+    const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * BQ > a.Sq;
+    if (masked)
+      compute(std::true_type{}, qt);
+    else
+      compute(std::false_type{}, qt);
+    __syncthreads();                                          // (B) dS^T visible
+    // dQ_acc += dS K: wave w takes query block mb and d block db; contraction over the
+    // 128 keys, slots = keys 16kc + 8g + j; A = dS by transpose reads of dS^T (the
+    // 16-lane group reads 4 keys x 16 queries), B = K^T rows; result lane = d
+    // column, regs = queries.
     {
       constexpr int NBLK = MB * DB;                          // (query block, d block) pairs
-      const T* sds = lds + L::DS;
-      const T* kt = lds + L::KT;
+      const uint8_t* dstl = lds + L::DST;
+      const T* kt = reinterpret_cast<const T*>(lds + L::KT);
       float* dqb = a.dq_acc + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
       for (int blk = w; blk < NBLK; blk += 4) {
         const int mb = blk / DB;
         const int db = blk % DB;
         f32x16 acc = f32x16{};
+        const int qcol = 32 * mb + 16 * hsel + 4 * (s16 & 3);
 #pragma unroll
         for (int kc = 0; kc < kBKV / 16; ++kc) {
-          const V8 av = as_v8<V8>(ld_lds_16(sds + (32 * mb + n) * L::SSTR + 16 * kc + 8 * grp));
+          const int kr0 = 16 * kc + 8 * grp + (s16 >> 2);
+          const u32x2 lo = tr_read(dstl + (kr0 * BQ + qcol) * 2);
+          const u32x2 hi = tr_read(dstl + ((kr0 + 4) * BQ + qcol) * 2);
+          const V8 av = as_v8<V8>(u32x4{lo.x, lo.y, hi.x, hi.y});
           const V8 bv = as_v8<V8>(ld_lds_16(kt + (32 * db + n) * L::KSTR + 16 * kc + 8 * grp));
           acc = E::mfma(av, bv, acc);
         }
@@ -378,7 +409,6 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();                                          // (C) stage reusable
   }
 
   // dK = scale * sum dS^T Q, dV = sum P^T dO; lane = d column, regs = keys.
