@@ -13,18 +13,21 @@
 //      fixed order);
 //   3. convert: dQ = scale * accumulator in the requested gradient type.
 //
-// Wave layout of the main kernel (4 waves, BKV = 128 keys, wave w owns keys
-// 32w .. 32w+31 of the tile).  S and dP are computed un-transposed on the 32x32x16
-// matrix core with the query rows as M and the wave's keys as N, so each lane holds
-// ONE key and 16 query rows of it: exactly the A-operand shape that dV += P^T dO and
-// dK += dS^T Q need, with no data movement.  Their B operands (dO and Q with the
-// query index as the contraction) come from the row-major staged tiles through
-// ds_read_b64_tr_b16 (one column of 4 consecutive rows per lane).  dQ needs dS with
-// queries as rows: dS goes to LDS key-major (8-byte writes of 4 queries) and comes
-// back through the same transpose read; each wave then forms one (query block, d
-// block) of dS K over all 128 keys.  Staged rows are unpadded, their 16-byte chunks
-// XOR-swizzled so that both the 16-byte fragment reads and the transpose reads of a
-// tile hit distinct banks.
+// Wave layout of the main kernel: 8 waves, BKV = 128 keys, wave w owns keys
+// 16w .. 16w+15 of the tile, on the 16x16x32 matrix core (A lane l = row l%16,
+// contraction slots from group l/16; B lane l = column l%16, same slots; C lane l =
+// column l%16, rows 4(l/16) .. +3).  Sixteen keys per wave keep each wave's dK and
+// dV accumulators at 64 registers, so two waves share each SIMD.  S and dP are
+// computed with the queries (two 16-row tiles of the 32-query step) as M and the
+// wave's keys as N, so each lane holds ONE key and 4 + 4 query rows of it: the
+// A-operand shape of dV += P^T dO and dK += dS^T Q (slots = queries 4g+i and
+// 16+4g+i).  Their B operands (dO and Q with the query index as the contraction) come
+// from the row-major staged tiles through ds_read_b64_tr_b16 (one column of 4
+// consecutive rows per lane).  dQ needs dS with queries as rows: dS goes to LDS
+// key-major (8-byte writes of 4 queries) and comes back through the same transpose
+// read, against K (row-major in LDS, transpose-read with keys as the contraction).
+// Staged rows are unpadded, their 16-byte chunks XOR-swizzled so that the 16-byte
+// fragment reads and the transpose reads of a tile both hit distinct banks.
 #include <type_traits>
 
 #include "../../include/attn.h"
@@ -35,7 +38,8 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kNT = 256;
+constexpr int kNT = 256;      // preprocess / convert kernels
+constexpr int kNTM = 512;     // main kernel: 8 waves
 constexpr int kBKV = 128;
 
 // ---------------------------------------------------------------------------------
@@ -88,12 +92,54 @@ template <typename G> __device__ inline void store_grad(G* p, float x) { *p = (G
 template <typename T> constexpr bool kSplit = false;
 template <> constexpr bool kSplit<bf16> = true;
 
-// Pack 8 floats into 8 element values (hi) and, for bf16, the 8 residuals x - hi (lo).
+// ---------------------------------------------------------------------------------
+// 2. main column-owner kernel
+//
+// Chunk swizzle of rows staged in LDS (16-byte chunk p of row r at p ^ swz(r)):
+//  * fragment reads: 16 consecutive rows, one chunk per 16 lanes -> 16 bank groups;
+//  * transpose reads: 8 consecutive rows x 2 chunks per 32 lanes -> 16 bank groups.
+// Rows of 128 bytes (d = 64) pair up in one 256-byte bank span.
+template <int D> __device__ inline int swz_row(int r) {
+  if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+  return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
+template <int D>
+struct BwdLds {
+  static constexpr int BQ = 32;               // queries per step
+  static constexpr int ROWB = D * 2;          // staged row bytes
+  static constexpr int Q = 0;                 // byte offsets
+  static constexpr int DO = Q + BQ * ROWB;
+  static constexpr int DST = DO + BQ * ROWB;  // dS^T [key][query], 16-bit, 64-byte rows
+  static constexpr int K = DST + kBKV * BQ * 2;   // K tile, row-major
+  static constexpr int V = K + kBKV * ROWB;       // V tile, row-major
+  static constexpr int BYTES = V + kBKV * ROWB;
+};
+
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ inline u32x2 tr_read(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+}
+
+template <typename T> struct M16;
+template <> struct M16<f16> {
+  static __device__ inline f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct M16<bf16> {
+  static __device__ inline f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+// Pack 8 floats (two groups of 4) into element values (hi) and, for bf16, the
+// residuals x - hi (lo).
 template <typename T>
-__device__ inline void split_pack8(const f32x16& x, int off, u32x4& hi, u32x4& lo) {
-  float r[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = x[off + j];
+__device__ inline void split_pack4x2(const f32x4& x0, const f32x4& x1, u32x4& hi, u32x4& lo) {
+  const float r[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   hi.x = Elem<T>::pack2(r[0], r[1]);
   hi.y = Elem<T>::pack2(r[2], r[3]);
   hi.z = Elem<T>::pack2(r[4], r[5]);
@@ -115,49 +161,18 @@ __device__ inline void split_pack8(const f32x16& x, int off, u32x4& hi, u32x4& l
   }
 }
 
-// ---------------------------------------------------------------------------------
-// 2. main column-owner kernel
-//
-// Chunk swizzle of the staged Q / dO rows (chunk p of row r at p ^ swz(r)):
-//  * 16-byte fragment reads: 16 consecutive rows, one chunk -> 16 distinct banks groups;
-//  * transpose reads: 4 consecutive rows x 4 consecutive chunks -> 16 distinct groups.
-template <int D> __device__ inline int swz_q(int r) {
-  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-  const int k = (r >> 1) & 7;   // rows of 128 bytes: pairs of rows share a 256-byte bank span
-  return (k >> 1) | ((k & 1) << 2);
-}
-
-template <int D, int BQ>
-struct BwdLds {
-  static constexpr int ROWB = D * 2;          // staged row bytes
-  static constexpr int Q = 0;                 // byte offsets
-  static constexpr int DO = Q + BQ * ROWB;
-  static constexpr int DST = DO + BQ * ROWB;  // dS^T [key][query], 16-bit
-  static constexpr int KSTR = kBKV + 8;       // K^T [d][key] stride (elements)
-  static constexpr int KT = DST + kBKV * BQ * 2;
-  static constexpr int BYTES = KT + D * KSTR * 2;
-};
-
-typedef __attribute__((ext_vector_type(4))) short i16x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ inline u32x2 tr_read(const uint8_t* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
-}
-
 template <typename T, typename G, int D, bool CAUSAL>
-__global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
-  typedef Elem<T> E;
-  typedef typename E::v8 V8;
-  constexpr int BQ = (D == 128) ? 32 : 64;
-  constexpr int MB = BQ / 32;               // query blocks of 32 per tile
-  constexpr int KC = D / 16;                // contraction chunks over d
-  constexpr int QC = BQ / 16;               // contraction chunks over queries
-  constexpr int DB = D / 32;                // d blocks of 32
-  constexpr int CPR = D / 8;                // 16-byte chunks per staged row
-  constexpr int SCH = BQ * CPR / (kNT / 2); // chunks per staging thread (Q or dO)
-  typedef BwdLds<D, BQ> L;
-  static_assert(SCH * (kNT / 2) == BQ * CPR, "staging chunks split evenly");
+__global__ __launch_bounds__(kNTM) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_main_kernel(BwdArgs a) {
+  typedef M16<T> MF;
+  typedef BwdLds<D> L;
+  constexpr int BQ = L::BQ;
+  constexpr int KC = D / 32;                // contraction chunks of 32 over d
+  constexpr int DB = D / 16;                // 16-wide d blocks of dK / dV / dQ
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int SCH = BQ * CPR / (kNTM / 2);   // staging chunks per thread (Q or dO)
+  constexpr int KCH = kBKV * CPR / kNTM;       // K-tile chunks per thread
+  static_assert(SCH >= 1 && SCH * (kNTM / 2) == BQ * CPR, "staging chunks split evenly");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
   __shared__ __attribute__((aligned(16))) float s_lse[BQ];
@@ -166,10 +181,8 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int n = lane & 31;
-  const int grp = lane >> 5;
-  const int s16 = lane & 15;
-  const int hsel = (lane >> 4) & 1;          // 16-lane group within the 32-lane half
+  const int n = lane & 15;
+  const int g = lane >> 4;
 
   const int jt = blockIdx.x;                 // key tile
   const int bkv = blockIdx.y;
@@ -182,51 +195,29 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
 
   const T* kbase = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
   const T* vbase = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)a.Sk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)a.Sk * D * 2);
 
-  // This wave's 32 keys as MFMA B operands (lane column = key, slots = d 16kc+8g..).
-  const int mykey = k0 + 32 * w + n;
-  V8 kf[KC], vf[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-    if (mykey < a.Sk) {
-      rk = ld_global_16(kbase + (int64_t)mykey * D + 16 * kc + 8 * grp);
-      rv = ld_global_16(vbase + (int64_t)mykey * D + 16 * kc + 8 * grp);
-    }
-    kf[kc] = as_v8<V8>(rk);
-    vf[kc] = as_v8<V8>(rv);
-  }
-  // K^T of the whole tile into LDS ([d][key]) for the dQ product: 4-key x 8-d blocks.
+  // The K and V tiles, row-major, in LDS (keys past S_k read as zero): the B operands
+  // of S and dP (column = key, slots d 32kc + 8g ..) and the K operand of dQ.
+  const int mykey = k0 + 16 * w + n;
   {
-    T* kt = reinterpret_cast<T*>(lds + L::KT);
-    for (int blk = tid; blk < (kBKV / 4) * (D / 8); blk += kNT) {
-      const int kq = blk / (D / 8);
-      const int dc = blk % (D / 8);
-      u32x4 r[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = k0 + 4 * kq + s;
-        r[s] = u32x4{0u, 0u, 0u, 0u};
-        if (key < a.Sk) r[s] = ld_global_16(kbase + (int64_t)key * D + dc * 8);
-      }
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        u32x2 ev, od;
-        ev.x = pack_lo(r[0][wd], r[1][wd]);
-        ev.y = pack_lo(r[2][wd], r[3][wd]);
-        od.x = pack_hi(r[0][wd], r[1][wd]);
-        od.y = pack_hi(r[2][wd], r[3][wd]);
-        st_lds_8(kt + (dc * 8 + 2 * wd) * L::KSTR + 4 * kq, ev);
-        st_lds_8(kt + (dc * 8 + 2 * wd + 1) * L::KSTR + 4 * kq, od);
-      }
+    for (int r = 0; r < KCH; ++r) {
+      const int idx = r * kNTM + tid;
+      const int row = idx / CPR;
+      const uint32_t src = (uint32_t)((k0 + row) * D + 8 * (idx % CPR)) * 2;
+      const int dst = row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16);
+      st_lds_16(lds + L::K + dst, buf_load_16(krs, src));
+      st_lds_16(lds + L::V + dst, buf_load_16(vrs, src));
     }
   }
 
-  f32x16 dk[DB], dv[DB];
+  f32x4 dk[DB], dv[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
+    dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const ColPlan cp = plan_cols(k0, k1, a.Sq, a.Sk, BQ, CAUSAL);
@@ -234,9 +225,9 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
   const int nsteps = nq * a.group;
 
   // Staging: the first half of the threads stages Q, the second dO; chunk idx =
-  // r * 128 + (tid % 128) of the tile is (row idx / CPR, chunk idx % CPR).
-  const bool stage_do = tid >= kNT / 2;
-  const int st_t = tid % (kNT / 2);
+  // r * 256 + (tid % 256) of the tile is (row idx / CPR, chunk idx % CPR).
+  const bool stage_do = tid >= kNTM / 2;
+  const int st_t = tid % (kNTM / 2);
   u32x4 sreg[SCH];
   float slse = 0.f, sdel = 0.f;
 
@@ -251,7 +242,7 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * 2);
 #pragma unroll
     for (int r = 0; r < SCH; ++r) {
-      const int idx = r * (kNT / 2) + st_t;
+      const int idx = r * (kNTM / 2) + st_t;
       sreg[r] = buf_load_16(rs, (uint32_t)((qt * BQ + idx / CPR) * D + 8 * (idx % CPR)) * 2);
     }
     if (tid < BQ) {
@@ -265,14 +256,28 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     uint8_t* dst = lds + (stage_do ? L::DO : L::Q);
 #pragma unroll
     for (int r = 0; r < SCH; ++r) {
-      const int idx = r * (kNT / 2) + st_t;
+      const int idx = r * (kNTM / 2) + st_t;
       const int row = idx / CPR;
-      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_q<D>(row)) * 16), sreg[r]);
+      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), sreg[r]);
     }
     if (tid < BQ) {
       s_lse[tid] = slse;
       s_del[tid] = sdel;
     }
+  };
+  // Transpose read of a staged row-major tile: the 16-lane group reads rows rb .. rb+3
+  // at columns c0 .. c0+15 (lane s addresses row rb + s/4, columns c0 + 4(s%4) .. +3);
+  // lane i receives column c0 + i of the 4 rows.
+  auto tr_tile = [&](const uint8_t* tile, int rb, int c0) -> u32x2 {
+    const int r = rb + (n >> 2);
+    const int col = c0 + 4 * (n & 3);
+    return tr_read(tile + r * L::ROWB + (((col >> 3) ^ swz_row<D>(r)) * 16) + (col & 7) * 2);
+  };
+  // dS^T rows are 64 bytes (4 units of 16): unit u of key row r sits at u ^ 2((r>>2)&1),
+  // so the 8 rows x 2 units of one 32-lane transpose-read pass hit distinct banks.
+  auto dst_off = [&](int key, int q) -> int {
+    const int u = q >> 3;
+    return key * (BQ * 2) + ((u ^ (2 * ((key >> 2) & 1))) * 16) + (q & 7) * 2;
   };
 
   // One step: S / dP for the wave's keys, P and dS, the dV / dK products, dS^T to LDS.
@@ -281,92 +286,83 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* sq = lds + L::Q;
     const uint8_t* sdo = lds + L::DO;
-    f32x16 s[MB], dp[MB];
+    // S, dP: tile t = query rows 16t .. 16t+15; lane holds queries 16t + 4g + i.  The
+    // K / V fragments of a contraction chunk serve both query tiles.
+    f32x4 s[2], dp[2];
+    const int krow = 16 * w + n;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int kc = 0; kc < KC; ++kc) {
+      const int koff = krow * L::ROWB + (((4 * kc + g) ^ swz_row<D>(krow)) * 16);
+      const u32x4 bk = ld_lds_16(lds + L::K + koff);
+      const u32x4 bv = ld_lds_16(lds + L::V + koff);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int row = 32 * mb + n;
-        const int off = row * L::ROWB + (((2 * kc + grp) ^ swz_q<D>(row)) * 16);
-        const V8 aq = as_v8<V8>(ld_lds_16(sq + off));
-        const V8 ad = as_v8<V8>(ld_lds_16(sdo + off));
-        s[mb] = E::mfma(aq, kf[kc], kc == 0 ? f32x16{} : s[mb]);
-        dp[mb] = E::mfma(ad, vf[kc], kc == 0 ? f32x16{} : dp[mb]);
+      for (int t = 0; t < 2; ++t) {
+        const int row = 16 * t + n;
+        const int off = row * L::ROWB + (((4 * kc + g) ^ swz_row<D>(row)) * 16);
+        const u32x4 aq = ld_lds_16(sq + off);
+        const u32x4 ad = ld_lds_16(sdo + off);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        s[t] = MF::run(aq, bk, kc == 0 ? z : s[t]);
+        dp[t] = MF::run(ad, bv, kc == 0 ? z : dp[t]);
       }
+      if (D == 128 && (kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
     }
     // P = exp2(S log2e scale - LSE log2e); dS = P (dP - D).
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int t = 0; t < 2; ++t) {
+      const int qb = 16 * t + 4 * g;
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&s_lse[qb]);
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[qb]);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qb = 32 * mb + 8 * r4 + 4 * grp;       // local query of regs 4r4..4r4+3
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&s_lse[qb]);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[qb]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * r4 + e;
-          float pv = fast_exp2(fmaf(s[mb][i], a.scale_log2, -lv[e]));
-          if constexpr (MASKED) {
-            const int qr = qt * BQ + qb + e;
-            const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
-            pv = vis ? pv : 0.f;
-          }
-          s[mb][i] = pv;
-          dp[mb][i] = pv * (dp[mb][i] - dl[e]);
+      for (int i = 0; i < 4; ++i) {
+        float pv = fast_exp2(fmaf(s[t][i], a.scale_log2, -lv[i]));
+        if constexpr (MASKED) {
+          const int qr = qt * BQ + qb + i;
+          const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
+          pv = vis ? pv : 0.f;
         }
+        s[t][i] = pv;
+        dp[t][i] = pv * (dp[t][i] - dl[i]);
       }
     }
-    // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries
-    // 16c + 8(j/4) + 4g + j%4 (registers 8(c%2) + j of query block c/2); B by
-    // transpose reads of the staged tiles: the 16-lane group reads 4 queries x 16 d
-    // (rows 16c + 4g, +8 for slots 4..7), lane s addressing row s/4, d 4(s%4).
-    // With bf16 elements P and dS enter as hi + lo pairs of bf16 values (x = hi + lo
-    // to about 16 significant bits), so these two sums keep float32-like precision.
+    // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries 4g + i and
+    // 16 + 4g + i; B = dO / Q columns by transpose reads of those rows.  With bf16
+    // elements P and dS enter as hi + lo pairs (x = hi + lo to about 16 significant
+    // bits), so these two sums keep float32-like precision.
+    u32x4 pp, pl, ss, sl;
+    split_pack4x2<T>(s[0], s[1], pp, pl);
+    split_pack4x2<T>(dp[0], dp[1], ss, sl);
 #pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      const int mb = c >> 1;
-      const int hb = (c & 1) * 8;
-      u32x4 pp, ss, pl, sl;
-      split_pack8<T>(s[mb], hb, pp, pl);
-      split_pack8<T>(dp[mb], hb, ss, sl);
-      const int r0 = 16 * c + 4 * grp + (s16 >> 2);
-      const int r1 = r0 + 8;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int col = 32 * db + 16 * hsel + 4 * (s16 & 3);
-        const int o0 = r0 * L::ROWB + (((col >> 3) ^ swz_q<D>(r0)) * 16) + (col & 7) * 2;
-        const int o1 = r1 * L::ROWB + (((col >> 3) ^ swz_q<D>(r1)) * 16) + (col & 7) * 2;
-        const u32x2 olo = tr_read(sdo + o0), ohi = tr_read(sdo + o1);
-        const u32x2 qlo = tr_read(sq + o0), qhi = tr_read(sq + o1);
-        const V8 ob = as_v8<V8>(u32x4{olo.x, olo.y, ohi.x, ohi.y});
-        const V8 qb4 = as_v8<V8>(u32x4{qlo.x, qlo.y, qhi.x, qhi.y});
-        dv[db] = E::mfma(as_v8<V8>(pp), ob, dv[db]);
-        dk[db] = E::mfma(as_v8<V8>(ss), qb4, dk[db]);
-        if (kSplit<T>) {
-          dv[db] = E::mfma(as_v8<V8>(pl), ob, dv[db]);
-          dk[db] = E::mfma(as_v8<V8>(sl), qb4, dk[db]);
-        }
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 olo = tr_tile(sdo, 4 * g, 16 * db), ohi = tr_tile(sdo, 16 + 4 * g, 16 * db);
+      const u32x2 qlo = tr_tile(sq, 4 * g, 16 * db), qhi = tr_tile(sq, 16 + 4 * g, 16 * db);
+      const u32x4 ob = {olo.x, olo.y, ohi.x, ohi.y};
+      const u32x4 qb4 = {qlo.x, qlo.y, qhi.x, qhi.y};
+      dv[db] = MF::run(pp, ob, dv[db]);
+      dk[db] = MF::run(ss, qb4, dk[db]);
+      if (kSplit<T>) {
+        dv[db] = MF::run(pl, ob, dv[db]);
+        dk[db] = MF::run(sl, qb4, dk[db]);
       }
+      // keep the operand reads of at most two d blocks in flight (registers)
+      if ((db & 1) == 1) __builtin_amdgcn_sched_barrier(0);
     }
-    // dS^T -> LDS [key][query]: registers 4r4 .. 4r4+3 are 4 consecutive queries.
-    uint8_t* dst = lds + L::DST;
-    const int krow = 32 * w + n;
+    // dS^T -> LDS [key][query]: registers 0..3 of tile t are queries 16t + 4g .. +3.
+    uint8_t* dsl = lds + L::DST;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        u32x2 pk;
-        pk.x = E::pack2(dp[mb][4 * r4 + 0], dp[mb][4 * r4 + 1]);
-        pk.y = E::pack2(dp[mb][4 * r4 + 2], dp[mb][4 * r4 + 3]);
-        st_lds_8(dst + (krow * BQ + 32 * mb + 8 * r4 + 4 * grp) * 2, pk);
-      }
+    for (int t = 0; t < 2; ++t) {
+      u32x2 pk;
+      pk.x = Elem<T>::pack2(dp[t][0], dp[t][1]);
+      pk.y = Elem<T>::pack2(dp[t][2], dp[t][3]);
+      st_lds_8(dsl + dst_off(krow, 16 * t + 4 * g), pk);
+    }
   };
 
   if (nsteps > 0) prefetch(0);
   for (int step = 0; step < nsteps; ++step) {
     int h, qt;
     step_coords(step, h, qt);
-    // The previous step's reads of the staged tiles ended before its barrier (B), and
+    // (The first barrier (A) also publishes the K and V tiles.)  The previous step's reads of the staged tiles ended before its barrier (B), and
     // this step's dS^T writes come after barrier (A): one barrier pair per step.
     store_stage();
     __syncthreads();                                          // (A) stage visible
@@ -378,48 +374,47 @@ __global__ __launch_bounds__(kNT) void bwd_main_kernel(BwdArgs a) {
     else
       compute(std::false_type{}, qt);
     __syncthreads();                                          // (B) dS^T visible
-    // dQ_acc += dS K: wave w takes query block mb and d block db; contraction over the
-    // 128 keys, slots = keys 16kc + 8g + j; A = dS by transpose reads of dS^T (the
-    // 16-lane group reads 4 keys x 16 queries), B = K^T rows; result lane = d
-    // column, regs = queries.
+    // dQ_acc += dS K over the 128 keys: block (query tile tq, d block db) per wave pass;
+    // slots = keys 32kc + 4g + i and 32kc + 16 + 4g + i for both operands (A = dS by
+    // transpose reads of dS^T, B = K by transpose reads of the K tile); result lane =
+    // d column, regs = queries 16tq + 4g + i.
     {
-      constexpr int NBLK = MB * DB;                          // (query block, d block) pairs
-      const uint8_t* dstl = lds + L::DST;
-      const T* kt = reinterpret_cast<const T*>(lds + L::KT);
+      const uint8_t* dsl = lds + L::DST;
+      const uint8_t* kt = lds + L::K;
       float* dqb = a.dq_acc + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
-      for (int blk = w; blk < NBLK; blk += 4) {
-        const int mb = blk / DB;
+      for (int blk = w; blk < 2 * DB; blk += 8) {
+        const int tq = blk / DB;
         const int db = blk % DB;
-        f32x16 acc = f32x16{};
-        const int qcol = 32 * mb + 16 * hsel + 4 * (s16 & 3);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kc = 0; kc < kBKV / 16; ++kc) {
-          const int kr0 = 16 * kc + 8 * grp + (s16 >> 2);
-          const u32x2 lo = tr_read(dstl + (kr0 * BQ + qcol) * 2);
-          const u32x2 hi = tr_read(dstl + ((kr0 + 4) * BQ + qcol) * 2);
-          const V8 av = as_v8<V8>(u32x4{lo.x, lo.y, hi.x, hi.y});
-          const V8 bv = as_v8<V8>(ld_lds_16(kt + (32 * db + n) * L::KSTR + 16 * kc + 8 * grp));
-          acc = E::mfma(av, bv, acc);
+        for (int kc = 0; kc < kBKV / 32; ++kc) {
+          const int kb0 = 32 * kc + 4 * g + (n >> 2);
+          const int qcol = 16 * tq + 4 * (n & 3);
+          const u32x2 alo = tr_read(dsl + dst_off(kb0, qcol));
+          const u32x2 ahi = tr_read(dsl + dst_off(kb0 + 16, qcol));
+          const u32x2 blo = tr_tile(kt, 32 * kc + 4 * g, 16 * db);
+          const u32x2 bhi = tr_tile(kt, 32 * kc + 16 + 4 * g, 16 * db);
+          acc = MF::run(u32x4{alo.x, alo.y, ahi.x, ahi.y}, u32x4{blo.x, blo.y, bhi.x, bhi.y}, acc);
         }
-        const int dcol = 32 * db + n;
+        const int dcol = 16 * db + n;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qr = qt * BQ + 32 * mb + 8 * (i >> 2) + 4 * grp + (i & 3);
+        for (int i = 0; i < 4; ++i) {
+          const int qr = qt * BQ + 16 * tq + 4 * g + i;
           if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, acc[i]);
         }
       }
     }
   }
 
-  // dK = scale * sum dS^T Q, dV = sum P^T dO; lane = d column, regs = keys.
+  // dK = scale * sum dS^T Q, dV = sum P^T dO; lane = d column, regs = keys 4g + i.
   G* dkb = reinterpret_cast<G*>(a.dk) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
   G* dvb = reinterpret_cast<G*>(a.dv) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    const int dcol = 32 * db + n;
+    const int dcol = 16 * db + n;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = k0 + 32 * w + 8 * (i >> 2) + 4 * grp + (i & 3);
+    for (int i = 0; i < 4; ++i) {
+      const int key = k0 + 16 * w + 4 * g + i;
       if (key < a.Sk) {
         store_grad<G>(dkb + (int64_t)key * D + dcol, dk[db][i] * a.scale);
         store_grad<G>(dvb + (int64_t)key * D + dcol, dv[db][i]);
@@ -437,9 +432,9 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.Sk + kBKV - 1) / kBKV), (unsigned)(a.B * a.Hkv));
   if (a.causal)
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true>), grid, dim3(kNT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true>), grid, dim3(kNTM), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false>), grid, dim3(kNT), 0, stream, a);
+    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false>), grid, dim3(kNTM), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n4 = rows * D / 4;
