@@ -26,6 +26,8 @@
 // V^T is stored in LDS with the keys of each d row permuted so that the 32 keys a lane
 // group needs for one 64-key contraction are 32 contiguous bytes: key k lives at byte
 // 32 * ((k >> 2) & 1) + ((k >> 3) << 2) + (k & 3) of its row.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 #include "tile_plan.h"
@@ -67,10 +69,18 @@ __device__ inline u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max over the two lanes l and l ^ 32 (one VALU lane swap).
+__device__ inline float max_pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ inline int vt_pos(int k) { return 32 * ((k >> 2) & 1) + ((k >> 3) << 2) + (k & 3); }
 
 template <int NW, bool OF32>
-__global__ __launch_bounds__(NW * kWave) void fp8_fwd_kernel(Fp8Args a) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void fp8_fwd_kernel(Fp8Args a) {
   typedef Fp8Lds L;
   constexpr int NT = NW * kWave;
   constexpr int BQ = NW * 32;
@@ -105,6 +115,10 @@ __global__ __launch_bounds__(NW * kWave) void fp8_fwd_kernel(Fp8Args a) {
   const int qrow = q0 + w * 32 + n;
   const TilePlan plan = plan_rows(q0, min(q0 + BQ, a.Sq), a.Sq, a.Sk, BC, 0);
   const float dq = qrow < a.Sq ? a.q_scale[(int64_t)(b * a.Hq + h) * nqb + qrow / SCALE_ROWS] : 0.f;
+  // score factor without the K descale; a negative score scale is moved into Q (sign
+  // flip of the bf16 operand) so that the factor is >= 0
+  const float c_q = fabsf(a.scale_log2) * dq;
+  const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   // Q^T fragments (bf16 B operand): lane column = query, slots = d 16kc+8g .. +8.
   bf16x8 qf[D / 16];
@@ -112,7 +126,12 @@ __global__ __launch_bounds__(NW * kWave) void fp8_fwd_kernel(Fp8Args a) {
   for (int kc = 0; kc < D / 16; ++kc) {
     u32x2 raw = {0u, 0u};
     if (qrow < a.Sq) raw = *reinterpret_cast<const u32x2*>(qb + (int64_t)qrow * D + 16 * kc + 8 * grp);
-    qf[kc] = as_v8<bf16x8>(e4m3x8_to_bf16(raw.x, raw.y));
+    u32x4 wide = e4m3x8_to_bf16(raw.x, raw.y);
+    wide.x ^= qsign;
+    wide.y ^= qsign;
+    wide.z ^= qsign;
+    wide.w ^= qsign;
+    qf[kc] = as_v8<bf16x8>(wide);
   }
 
   f32x16 o[D / 32];
@@ -189,62 +208,78 @@ __global__ __launch_bounds__(NW * kWave) void fp8_fwd_kernel(Fp8Args a) {
     }
   };
 
-  auto compute_tile = [&](int t, int stage) {
+  // One K/V tile.  MASKED applies the key-tail mask (only the tiles the plan marks).
+  auto compute_tile = [&](auto masked_tag, int t, int stage) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* ks = lds + stage * L::STAGE;
     const uint8_t* vs = ks + L::K_BYTES;
     const float dk = ksc[(t * BC) / SCALE_ROWS];
     const float dv = vsc[(t * BC) / SCALE_ROWS];
     f32x16 s[2];
-    s[0] = f32x16{};
-    s[1] = f32x16{};
     const bf16* kbf = reinterpret_cast<const bf16*>(ks);
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
         const bf16x8 av = as_v8<bf16x8>(ld_lds_16(kbf + (kbk * 32 + n) * L::KSTR + 16 * kc + 8 * grp));
-        s[kbk] = Elem<bf16>::mfma(av, qf[kc], s[kbk]);
+        s[kbk] = Elem<bf16>::mfma(av, qf[kc], kc == 0 ? f32x16{} : s[kbk]);
       }
+      if ((kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
     }
-    const float csc = a.scale_log2 * dq * dk;        // descales before the row max
-    const bool masked = t >= plan.first_masked;
-    float mx = -INFINITY;
+    // Descales before the row max: x = csc * s with csc = scale log2(e) dQ dK.  The max
+    // is taken on the raw accumulators (csc >= 0: descales are positive and a negative
+    // score scale is moved into Q), so x enters only through one FMA below.
+    const float csc = c_q * dk;
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) {
+      for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kbk][i] * csc;
-        if (masked) {
+        for (int i = 0; i < 16; ++i) {
           const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
-          x = key < a.Sk ? x : -INFINITY;
+          s[kbk][i] = key < a.Sk ? s[kbk][i] : -INFINITY;
         }
-        s[kbk][i] = x;
-        mx = fmaxf(mx, x);
-      }
     }
-    mx = wave_max_xor32(mx);
+    float r0 = vmax(s[0][0], s[0][1]), r1 = vmax(s[0][2], s[0][3]);
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int i = (kbk == 0 ? 4 : 0); i < 16; i += 4) {
+        r0 = vmax(r0, vmax(s[kbk][i], s[kbk][i + 1]));
+        r1 = vmax(r1, vmax(s[kbk][i + 2], s[kbk][i + 3]));
+      }
+    const float mr = vmax(r0, r1);
+    const float mx = max_pair32(mr == -INFINITY ? -INFINITY : mr * csc);
     const float m_new = fmaxf(m_i, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_i - m_use);
     const float m_off = m_use - 8.f;                 // u = 2^8 exp2(x - m)
-    float rs = 0.f;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float u = fast_exp2(s[kbk][i] - m_off);
-        s[kbk][i] = u;
-        rs += u;
+      for (int i = 0; i < 16; i += 2) {
+        // masked cells hold -inf: fma(-inf, csc, .) = -inf -> u = 0 (csc > 0)
+        const float u0 = fast_exp2(fmaf(s[kbk][i], csc, -m_off));
+        const float u1 = fast_exp2(fmaf(s[kbk][i + 1], csc, -m_off));
+        s[kbk][i] = u0;
+        s[kbk][i + 1] = u1;
+        rs0 += u0;
+        rs1 += u1;
       }
     }
-    l_i = alpha * l_i + rs;
+    l_i = alpha * l_i + (rs0 + rs1);
     m_i = m_new;
+    // The accumulator is kept in units of the current V descale s_v: moving to a tile
+    // with descale dv (and a moved max) multiplies it by alpha s_v / dv, skipped when
+    // that is 1 in every lane (same scale block, unmoved max).
     const float beta = alpha * (s_v / dv);
     s_v = dv;
+    if (wave_any(beta != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+      for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= beta;
+        for (int i = 0; i < 16; ++i) o[db][i] *= beta;
+      }
     }
     // P^T as the fp8 B operand: slot j = register (j % 16) of key block j / 16.
     i32x8 pb;
@@ -274,7 +309,10 @@ __global__ __launch_bounds__(NW * kWave) void fp8_fwd_kernel(Fp8Args a) {
   for (int t = 0; t < nt; ++t) {
     const int stage = t & 1;
     if (t + 1 < nt) load_tile(t + 1);
-    compute_tile(t, stage);
+    if (t >= plan.first_masked)
+      compute_tile(std::true_type{}, t, stage);
+    else
+      compute_tile(std::false_type{}, t, stage);
     if (t + 1 < nt) store_tile(stage ^ 1);
     __syncthreads();
   }
