@@ -16,6 +16,10 @@ Recipe (every draw is reproducible from its seed):
     float32 descale per (batch, head, 128-row block): scale = amax / 448 (1 if the
     block is all zero) and code = e4m3fn(x / scale) by torch's cast.  The
     quantisation is input preparation: the attention path receives codes + scales.
+  * packed variable-length prefill: token-major q [total_q, H_q, d] and k/v
+    [total_k, H_kv, d] with int32 cumulative offsets cu_q, cu_k [B+1].
+  * paged decode: K/V pools [num_pages, H_kv, P, d] with a seeded random permutation
+    of the pages as the int32 block table [B, max_pages]; unused pages hold draws too.
 """
 from __future__ import annotations
 
@@ -127,6 +131,45 @@ def fp8_prefill(B, Hq, Hkv, Sq, Sk, d, seed, block=FP8_BLOCK_ROWS) -> Workload:
 
 
 # The five workloads the library is measured on, with their sizes.
+def varlen_prefill(seqlens_q, seqlens_k, Hq, Hkv, d, dtype, seed, causal=False, scale=None) -> Workload:
+    """Packed token-major q [sum Sq, Hq, d], k/v [sum Sk, Hkv, d] + cu_q, cu_k [B+1] int32."""
+    sq = np.asarray(seqlens_q, dtype=np.int64)
+    sk = np.asarray(seqlens_k, dtype=np.int64)
+    cq = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
+    t = {
+        "q": normal((int(cq[-1]), Hq, d), seed, 0, dtype),
+        "k": normal((int(ck[-1]), Hkv, d), seed, 1, dtype),
+        "v": normal((int(ck[-1]), Hkv, d), seed, 2, dtype),
+        "cu_q": torch.from_numpy(cq.copy()),
+        "cu_k": torch.from_numpy(ck.copy()),
+    }
+    p = dict(B=len(sq), Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, causal=bool(causal),
+             max_seqlen_q=int(sq.max()) if len(sq) else 0, max_seqlen_k=int(sk.max()) if len(sk) else 0,
+             scale=float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale)))
+    return Workload(f"varlen_{dtype}_B{len(sq)}x{Hq}x{Hkv}x{d}", t, p)
+
+
+def paged_decode(B, Hq, Hkv, d, dtype, seed, page_size, lo=1024, hi=32768, chunk=256, lengths=None,
+                 spare_pages=3) -> Workload:
+    """q [B,Hq,1,d]; K/V pools [num_pages, Hkv, P, d]; block table [B, max_pages] int32
+    (a seeded random permutation of all pages); seqlens int32 [B]."""
+    lens = decode_lengths(seed, B, lo, hi) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    maxp = max(1, -(-int(lens.max()) // page_size)) if len(lens) else 1
+    npages = B * maxp + spare_pages
+    perm = _rng(seed, 5).permutation(npages)[:B * maxp].astype(np.int32)
+    t = {
+        "q": normal((B, Hq, 1, d), seed, 0, dtype),
+        "k_pages": normal((npages, Hkv, page_size, d), seed, 1, dtype),
+        "v_pages": normal((npages, Hkv, page_size, d), seed, 2, dtype),
+        "block_table": torch.from_numpy(perm.reshape(B, maxp).copy()),
+        "seqlens": torch.from_numpy(lens.copy()),
+    }
+    p = dict(B=B, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, page_size=page_size, max_pages=maxp, num_pages=npages,
+             chunk=chunk, scale=float(np.float32(1.0 / math.sqrt(d))))
+    return Workload(f"paged_decode_{dtype}_{B}x{Hq}x{Hkv}x{d}_P{page_size}", t, p)
+
+
 CONFIGS = {
     "c1_fp16_fwd_small": lambda: prefill(1, 4, 4, 128, 128, 64, "f16", seed=1),
     "c2_fp16_fwd": lambda: prefill(1, 8, 8, 4096, 4096, 64, "f16", seed=2),

@@ -13,11 +13,12 @@ Sources (page titles of the reference text):
           the Moving Bottleneck"
 
 Modules:
-  dense   -- the dense definition (forward, LSE, backward, decode)   [pinned]
+  dense   -- the dense definition (forward, LSE, backward, decode), its
+             packed variable-length form and the paged-cache decode       [pinned]
   state   -- the online (m, l, u, n) state algebra and its merges     [pinned]
   fp8     -- the E4M3FN codebook and the quantised forward steps      [codebook,
              the 2^8 cancellation and the no-rounding reduction are pinned;
              parity of the quantised output itself is unpinned: no printed values
              exist for this input distribution]
-  tiles   -- causal tile classes and visit counts                    [pinned]
+  tiles   -- causal tile classes, visit counts, packed-launch census  [pinned]
 """

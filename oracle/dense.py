@@ -169,3 +169,68 @@ def decode(q, k_cache, v_cache, seqlens, scale: float, batches=None):
         n = int(lens[b])
         O[b:b + 1], LSE[b:b + 1] = forward(Q[b:b + 1], K[b:b + 1, :, :n], V[b:b + 1, :, :n], scale, False)
     return O, LSE
+
+
+def _seq_lengths(cu):
+    cu = np.asarray(cu.cpu() if hasattr(cu, "cpu") else cu).astype(np.int64)
+    return cu, cu[1:] - cu[:-1]
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool = False, seqs=None):
+    """Packed variable-length forward ([FA2] section 0x06F: each packed sequence has
+    its own query and key extents, causal alignment and tile classes).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d] token-major; cu_q, cu_k int [B+1]
+    cumulative offsets.  Sequence b is the dense definition above on its own rows
+    cu_q[b] .. cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1.
+    Returns (O [total_q, Hq, dv], LSE [Hq, total_q]) float64.
+    """
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    cq, nq = _seq_lengths(cu_q)
+    ck, nk = _seq_lengths(cu_k)
+    O = np.full((Q.shape[0], Q.shape[1], V.shape[2]), np.nan)
+    LSE = np.full((Q.shape[1], Q.shape[0]), np.nan)
+    for b in (range(len(nq)) if seqs is None else seqs):
+        qb = Q[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None]        # [1, Hq, Sq_b, d]
+        kb = K[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+        vb = V[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None]
+        ob, lb = forward(qb, kb, vb, scale, causal)
+        O[cq[b]:cq[b + 1]] = ob[0].transpose(1, 0, 2)
+        LSE[:, cq[b]:cq[b + 1]] = lb[0]
+    return O, LSE
+
+
+def gather_pages(pages, block_table, seqlens):
+    """Logical K (or V) rows of each sequence from a paged pool.
+
+    pages [num_pages, H, P, d]; block_table int [B, max_pages]: logical page i of
+    sequence b is physical page block_table[b, i]; key j of sequence b is row j % P of
+    page block_table[b, j // P].  Returns a list of [H, seqlens[b], d] arrays.
+    """
+    X = _f64(pages)
+    bt = np.asarray(block_table.cpu() if hasattr(block_table, "cpu") else block_table).astype(np.int64)
+    lens = np.asarray(seqlens.cpu() if hasattr(seqlens, "cpu") else seqlens).astype(np.int64)
+    P = X.shape[2]
+    out = []
+    for b in range(len(lens)):
+        n = int(lens[b])
+        npg = -(-n // P)
+        rows = [X[bt[b, i]] for i in range(npg)]                 # each [H, P, d]
+        full = np.concatenate(rows, axis=1) if rows else np.zeros((X.shape[1], 0, X.shape[3]))
+        out.append(full[:, :n])
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale: float):
+    """One-query decode over a paged K/V pool: the contiguous decode above applied to
+    the gathered logical rows of each sequence.  Returns (O [B,Hq,1,dv], LSE [B,Hq,1])."""
+    Q = _f64(q)
+    Ks = gather_pages(k_pages, block_table, seqlens)
+    Vs = gather_pages(v_pages, block_table, seqlens)
+    B, Hq = Q.shape[:2]
+    O = np.full((B, Hq, 1, Vs[0].shape[2] if Vs else Q.shape[3]), np.nan)
+    LSE = np.full((B, Hq, 1), np.nan)
+    for b in range(B):
+        O[b:b + 1], LSE[b:b + 1] = forward(Q[b:b + 1], Ks[b][None], Vs[b][None], scale, False)
+    return O, LSE
+

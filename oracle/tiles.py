@@ -40,3 +40,24 @@ def visited_per_query_tile(sq, sk, br, bc, delta):
     """Number of non-skipped key tiles for each query tile."""
     return [sum(1 for k0, k1 in ranges(sk, bc) if tile_class(q0, q1, k0, k1, delta) != "skipped")
             for q0, q1 in ranges(sq, br)]
+
+
+def varlen_census(seqlens_q, seqlens_k, br, max_seqlen_q, n_heads):
+    """Workgroup populations of a packed launch ([FA2] section 0x04B): the grid is
+    ceil(max_seqlen_q / br) query tiles x sequences x heads; a workgroup is active when
+    its first row exists (i br < S_q) and the sequence has keys (S_k > 0), full when it
+    owns br valid rows, tail otherwise.  Row slots are br per active workgroup."""
+    ntiles = -(-max_seqlen_q // br)
+    out = {"launched": ntiles * len(seqlens_q) * n_heads, "active": 0, "full": 0, "tail": 0,
+           "row_slots": 0, "valid_rows": 0}
+    for sq, sk in zip(seqlens_q, seqlens_k):
+        for i in range(ntiles):
+            if i * br >= sq or sk == 0:
+                continue
+            rows = min(br, sq - i * br)
+            out["active"] += n_heads
+            out["full" if rows == br else "tail"] += n_heads
+            out["row_slots"] += br * n_heads
+            out["valid_rows"] += rows * n_heads
+    return out
+
