@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -41,18 +41,57 @@ def _require(t, name, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d CUDA tensor")
 
 
+def _expect(t, name, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
 def attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
     """O, LSE = attention(q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d]); fp16/bf16; LSE float32."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, n, 4)
     B, Hq, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
+    _expect(k, "k", (B, Hkv, Sk, d), q.dtype, q.device)
+    _expect(v, "v", (B, Hkv, Sk, d), q.dtype, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                         scale, int(bool(causal)), _code(q.dtype), _stream(stream))
     _lib.check("attn_fwd", st)
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                    causal=False, o=None, lse=None, stream=None):
+    """O [total_q, Hq, d], LSE [Hq, total_q] of packed token-major sequences
+    (q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_seqlens_* int32 [B+1] on the device)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, 3)
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _require(t, n, 1)
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    _expect(k, "k", (total_k, Hkv, d), q.dtype, q.device)
+    _expect(v, "v", (total_k, Hkv, d), q.dtype, q.device)
+    _expect(cu_seqlens_q, "cu_seqlens_q", (B + 1,), torch.int32, q.device)
+    _expect(cu_seqlens_k, "cu_seqlens_k", (B + 1,), torch.int32, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (Hq, total_q), torch.float32, q.device)
+    st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_k), B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k),
+                               total_q, total_k, d, scale, int(bool(causal)), _code(q.dtype), _stream(stream))
+    _lib.check("attn_fwd_varlen", st)
     return o, lse
 
 

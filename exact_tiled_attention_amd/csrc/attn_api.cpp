@@ -79,6 +79,42 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
 }
 
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                    float scale, int causal, attn_dtype_t dtype, void* stream) {
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_ERR_NULL;
+  if (total_q > 0 && (q == nullptr || o == nullptr)) return ATTN_ERR_NULL;
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 ||
+      total_k < 0)
+    return ATTN_ERR_SHAPE;
+  if (max_seqlen_q > kMaxSeq || max_seqlen_k > kMaxSeq || (int64_t)B * Hq > kMaxBH)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  // one sequence's rows (token stride H d), with a tile of tail rows past its end,
+  // must span less than 2 GiB: the kernels form 32-bit signed row offsets
+  if (((int64_t)max_seqlen_q + 256) * Hq * d * 2 >= ((int64_t)1 << 31) ||
+      ((int64_t)max_seqlen_k + 256) * Hkv * d * 2 >= ((int64_t)1 << 31))
+    return ATTN_ERR_SHAPE;
+  if (total_q == 0 || max_seqlen_q == 0) return ATTN_OK;   // no query row: nothing to write
+  FwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = max_seqlen_q; a.Sk = max_seqlen_k; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
+}
+
 int attn_fp8_kv_tile(void) { return attn_fp8_tile_keys(); }
 
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,

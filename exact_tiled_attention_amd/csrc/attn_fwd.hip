@@ -90,7 +90,7 @@ __device__ inline float max_pair32(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename T, int D, int QB, int RW, int KS, bool CAUSAL>
+template <typename T, int D, int QB, int RW, int KS, bool VL, bool CAUSAL>
 __global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
@@ -132,24 +132,50 @@ void fwd_kernel(FwdArgs a) {
   const int h = bh - b * a.Hq;
   const int kvh = h / a.group;
 
-  const T* qb = reinterpret_cast<const T*>(a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
-  const T* kb = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const T* vb = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, (uint32_t)a.Sq * D * 2);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)a.Sk * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)a.Sk * D * 2);
+  // Geometry of this (sequence, head): lengths, first-row element offsets, row strides
+  // (d for the padded layout, H d for the packed token-major layout), LSE row base.
+  // VL: the packed layout; otherwise the strides are the compile-time d.
+  int Sq, Sk;
+  int q_rs = D, kv_rs = D;
+  int64_t q_off, kv_off, lse_off;
+  if constexpr (VL) {
+    // extents clamped to the declared maxima and totals: inconsistent offsets can
+    // give wrong rows but never an access outside the tensors
+    const int tq = min(max(a.cu_q[b], 0), a.total_q);
+    const int tk = min(max(a.cu_k[b], 0), a.total_k);
+    Sq = min(min(max(a.cu_q[b + 1] - tq, 0), a.Sq), a.total_q - tq);
+    Sk = min(min(max(a.cu_k[b + 1] - tk, 0), a.Sk), a.total_k - tk);
+    q_rs = a.Hq * D;
+    kv_rs = a.Hkv * D;
+    q_off = ((int64_t)tq * a.Hq + h) * D;
+    kv_off = ((int64_t)tk * a.Hkv + kvh) * D;
+    lse_off = (int64_t)h * a.total_q + tq;
+  } else {
+    Sq = a.Sq;
+    Sk = a.Sk;
+    q_off = (int64_t)(b * a.Hq + h) * a.Sq * D;
+    kv_off = (int64_t)(b * a.Hkv + kvh) * a.Sk * D;
+    lse_off = (int64_t)(b * a.Hq + h) * a.Sq;
+  }
+  if (VL && qt * BQ >= Sq) return;   // whole workgroup, before any barrier
+  const T* qb = reinterpret_cast<const T*>(a.q) + q_off;
+  const T* kb = reinterpret_cast<const T*>(a.k) + kv_off;
+  const T* vb = reinterpret_cast<const T*>(a.v) + kv_off;
+  // range-checked spans: rows at or past the sequence end read as zero
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, Sq > 0 ? (uint32_t)((Sq - 1) * q_rs + D) * 2 : 0u);
+  const int64_t kv_bytes = Sk > 0 ? ((int64_t)(Sk - 1) * kv_rs + D) * 2 : 0;
 
   const int q0 = qt * BQ;
-  const int q1 = min(q0 + BQ, a.Sq);
-  const TilePlan plan = plan_rows(q0, q1, a.Sq, a.Sk, BC, CAUSAL);
+  const int q1 = min(q0 + BQ, Sq);
+  const TilePlan plan = plan_rows(q0, q1, Sq, Sk, BC, CAUSAL);
   const int w0 = q0 + w * QB * 32;
-  const int w1 = max(min(w0 + QB * 32, a.Sq), w0 + 1);
-  const TilePlan wplan = plan_rows(w0, w1, a.Sq, a.Sk, BC, CAUSAL);
+  const int w1 = max(min(w0 + QB * 32, Sq), w0 + 1);
+  const TilePlan wplan = plan_rows(w0, w1, Sq, Sk, BC, CAUSAL);
   int qrow[QB], klim[QB];   // this lane's query row per block; keys at or past klim are invisible
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     qrow[j] = w0 + 32 * j + n;
-    klim[j] = CAUSAL ? min(a.Sk, qrow[j] + (a.Sk - a.Sq) + 1) : a.Sk;
+    klim[j] = CAUSAL ? min(Sk, qrow[j] + (Sk - Sq) + 1) : Sk;
   }
 
   // Q^T fragments (B operand): lane column = its query row, slots = d 16kc+8g .. +8.
@@ -162,7 +188,7 @@ void fwd_kernel(FwdArgs a) {
   for (int j = 0; j < QB; ++j)
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      u32x4 raw = buf_load_16(qr, (uint32_t)(qrow[j] * D + 16 * kc + 8 * grp) * 2);
+      u32x4 raw = buf_load_16(qr, (uint32_t)(qrow[j] * q_rs + 16 * kc + 8 * grp) * 2);
       raw.x ^= qsign;
       raw.y ^= qsign;
       raw.z ^= qsign;
@@ -181,24 +207,40 @@ void fwd_kernel(FwdArgs a) {
   }
 
   // Staging: chunk idx = r * NTK + tid of a tile is LDS (row, pos) = (idx / CPR,
-  // idx % CPR) and holds global chunk pos ^ swz(row) of that row.
+  // idx % CPR) and holds global chunk pos ^ swz(row) of that row.  Load round r covers
+  // rows r*RS .. r*RS+RS-1 and the swizzles repeat every 16 rows, so a thread's
+  // column offset is the same in every round.  Padded layout: one resource over the
+  // head's rows, the row offsets are compile-time multiples of D.  Packed layout
+  // (runtime row stride): a per-round resource (uniform base and remaining range)
+  // with one shared vector offset, which keeps the stride products out of VGPRs.
+  constexpr int RS = NTK / TL::CPR;
+  static_assert(RS % 16 == 0 && NTK % TL::CPR == 0, "load rounds must cover whole swizzle periods");
   u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](u32x4 (&dst)[LOADS], __amdgpu_buffer_rsrc_t src, int t, bool is_v) {
+  const int trow = tid / TL::CPR, tpos = tid % TL::CPR;
+  const uint32_t co_k = (uint32_t)((tpos ^ TL::swz_k(trow)) * 16);
+  const uint32_t co_v = (uint32_t)((tpos ^ TL::swz_v(trow)) * 16);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)kv_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)kv_bytes);
+  auto load_tile = [&](u32x4 (&dst)[LOADS], const T* src, int t, bool is_v) {
+    const uint32_t co = is_v ? co_v : co_k;
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const int idx = r * NTK + tid;
-      const int row = idx / TL::CPR;
-      const int pos = idx % TL::CPR;
-      const int sw = is_v ? TL::swz_v(row) : TL::swz_k(row);
-      dst[r] = buf_load_16(src, (uint32_t)((t * BC + row) * D) * 2 + (uint32_t)((pos ^ sw) * 16));
+      if constexpr (VL) {
+        const int64_t off = (int64_t)(t * BC + r * RS) * kv_rs * 2;
+        const uint32_t left = kv_bytes > off ? (uint32_t)(kv_bytes - off) : 0u;
+        dst[r] = buf_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(src) + off, left),
+                             (uint32_t)(trow * kv_rs * 2) + co);
+      } else {
+        dst[r] = buf_load_16(is_v ? vr : kr, (uint32_t)((t * BC + r * RS + trow) * D * 2) + co);
+      }
     }
   };
   auto store_tile = [&](const u32x4 (&src)[LOADS], uint8_t* slot_base) {
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) st_lds_16(slot_base + (r * NTK + tid) * 16, src[r]);
   };
-  auto load_k = [&](int t) { load_tile(kreg, kr, t, false); };
-  auto load_v = [&](int t) { load_tile(vreg, vr, t, true); };
+  auto load_k = [&](int t) { load_tile(kreg, kb, t, false); };
+  auto load_v = [&](int t) { load_tile(vreg, vb, t, true); };
   auto store_k = [&](int slot) { store_tile(kreg, kring + slot * TL::BYTES); };
   auto store_v = [&](int slot) { store_tile(vreg, vring + slot * TL::BYTES); };
 
@@ -328,11 +370,11 @@ void fwd_kernel(FwdArgs a) {
   {
     u32x4 k0[LOADS], v0[LOADS], k1[LOADS];
     if (nr > 0) {
-      load_tile(k0, kr, tb, false);
-      load_tile(v0, vr, tb, true);
+      load_tile(k0, kb, tb, false);
+      load_tile(v0, vb, tb, true);
     }
     if (nr > 1) {
-      load_tile(k1, kr, tb + 1, false);
+      load_tile(k1, kb, tb + 1, false);
       load_v(tb + 1);
     }
     if (nr > 2) load_k(tb + 2);
@@ -452,8 +494,8 @@ void fwd_kernel(FwdArgs a) {
       const float l_tot = l_i[j] + __shfl_xor(l_i[j], 32);
       const bool empty = (m_i[j] == -INFINITY) || !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
-      if (qrow[j] < a.Sq) {
-        T* ob = reinterpret_cast<T*>(a.o) + ((int64_t)(b * a.Hq + h) * a.Sq + qrow[j]) * D;
+      if (qrow[j] < Sq) {
+        T* ob = reinterpret_cast<T*>(a.o) + q_off + (int64_t)qrow[j] * q_rs;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -465,7 +507,7 @@ void fwd_kernel(FwdArgs a) {
           }
         }
         if (a.lse != nullptr && grp == 0) {
-          a.lse[(int64_t)(b * a.Hq + h) * a.Sq + qrow[j]] = empty ? -INFINITY : (m_i[j] + __log2f(l_tot)) * ATTN_LN2;
+          a.lse[lse_off + qrow[j]] = empty ? -INFINITY : (m_i[j] + __log2f(l_tot)) * ATTN_LN2;
         }
       }
     }
@@ -479,10 +521,18 @@ hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   a.nqt = (a.Sq + BQ - 1) / BQ;
   const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
   const dim3 block(RW * KS * kWave);
-  if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false>), grid, block, 0, stream, a);
+  const bool vl = a.cu_q != nullptr;
+  if (a.causal) {
+    if (vl)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (vl)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -18,6 +18,12 @@ struct FwdArgs {
   int dtype_bf16;     // 1: bf16, 0: fp16
   float scale_log2;   // scale * log2(e)
   int nqt;            // query tiles (filled by the launcher)
+  // Packed variable-length layout (null cu_q: the padded [B, H, S, d] layout).  Q/O
+  // token-major [total_q, Hq, d], K/V [total_k, Hkv, d], LSE [Hq, total_q]; B is the
+  // number of sequences, Sq / Sk the longest ones.
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 struct Fp8Args {

@@ -78,6 +78,34 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fwd_varlen -- the forward of attn_fwd on packed variable-length sequences.
+ * "M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary", sections 0x04B
+ * (a packed launch covers the longest sequence; workgroups past a sequence's rows
+ * return at entry) and 0x06F (each packed sequence has its own query and key extents,
+ * causal alignment and tile classes; heads map as in attn_fwd).
+ *
+ *   q   [total_q, Hq,  d]  token-major, element type `dtype`                 (in)
+ *   k,v [total_k, Hkv, d]  token-major, element type `dtype`                 (in)
+ *   o   [total_q, Hq,  d]  element type `dtype`                              (out)
+ *   lse [Hq, total_q]      float32, natural log                    (out; may be NULL)
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B+1], nondecreasing, starting at 0;
+ *       sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and keys
+ *       cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1                                (in)
+ *   max_seqlen_q / max_seqlen_k: upper bounds of the per-sequence lengths (they size
+ *       the launch); total_q / total_k: rows of q and k.  Lengths beyond the bounds
+ *       or offsets beyond the totals are clamped: inconsistent metadata may give wrong
+ *       rows, never an access outside the tensors.
+ *   causal: bottom-right alignment per sequence (delta = S_k,b - S_q,b).
+ *   A sequence with no keys gives O = 0, LSE = -inf on its rows.  One sequence's rows
+ *   must span less than 2 GiB ((max_seqlen + 256) * H * d * 2 bytes: 32-bit signed row
+ *   offsets, including a tile of rows past the end), else ATTN_ERR_SHAPE.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,
+                    float scale, int causal, attn_dtype_t dtype, void* stream);
+
+/*
  * attn_fwd_fp8 -- forward on E4M3FN operands with per-block descales.
  * "M4.6 - FlashAttention-3/4 Hardware Pipelines", section 0x06 ("Derive Where Every
  * Scale Must Enter"; "Why The Source Raises Softmax Probabilities By 2^8"):

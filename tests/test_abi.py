@@ -58,6 +58,23 @@ def test_fwd_argument_checks():
     assert call(scale=float("inf")) == -8 and call(scale=float("nan")) == -8
 
 
+def test_fwd_varlen_argument_checks():
+    lib, _ = _lib()
+    f = lib.attn_fwd_varlen
+    def call(q=P, k=P, o=P, cuq=P, cuk=P, dtype=1, scale=0.125, **kw):
+        a = dict(B=2, Hq=4, Hkv=2, mq=16, mk=16, tq=20, tk=24, d=128)
+        a.update(kw)
+        return f(q, k, k, o, None, cuq, cuk, a["B"], a["Hq"], a["Hkv"], a["mq"], a["mk"], a["tq"], a["tk"],
+                 a["d"], scale, 1, dtype, None)
+    assert call(cuq=None) == -1 and call(cuk=None) == -1 and call(q=None) == -1 and call(k=None) == -1
+    assert call(B=0) == -2 and call(mq=-1) == -2 and call(tk=-1) == -2 and call(mq=1 << 21) == -2
+    assert call(Hq=64, mq=1 << 20) == -2                       # one sequence spans >= 4 GiB
+    assert call(Hq=3) == -3 and call(d=80) == -4 and call(dtype=2) == -5
+    assert call(scale=float("nan")) == -8
+    # nothing to compute: no launch, no dereference of the placeholders
+    assert call(tq=0, q=None, o=None) == 0 and call(mq=0) == 0
+
+
 def test_bwd_and_workspace_checks():
     lib, _ = _lib()
     ws = lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 64)
