@@ -130,7 +130,6 @@ def fp8_prefill(B, Hq, Hkv, Sq, Sk, d, seed, block=FP8_BLOCK_ROWS) -> Workload:
     return Workload(f"fp8_{B}x{Hq}x{Hkv}x{Sq}x{Sk}x{d}", t, p)
 
 
-# The five workloads the library is measured on, with their sizes.
 def varlen_prefill(seqlens_q, seqlens_k, Hq, Hkv, d, dtype, seed, causal=False, scale=None) -> Workload:
     """Packed token-major q [sum Sq, Hq, d], k/v [sum Sk, Hkv, d] + cu_q, cu_k [B+1] int32."""
     sq = np.asarray(seqlens_q, dtype=np.int64)
@@ -145,7 +144,7 @@ def varlen_prefill(seqlens_q, seqlens_k, Hq, Hkv, d, dtype, seed, causal=False, 
         "cu_k": torch.from_numpy(ck.copy()),
     }
     p = dict(B=len(sq), Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, causal=bool(causal),
-             max_seqlen_q=int(sq.max()) if len(sq) else 0, max_seqlen_k=int(sk.max()) if len(sk) else 0,
+             seqlens_q=sq.tolist(), seqlens_k=sk.tolist(), max_seqlen_q=int(sq.max()) if len(sq) else 0, max_seqlen_k=int(sk.max()) if len(sk) else 0,
              scale=float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale)))
     return Workload(f"varlen_{dtype}_B{len(sq)}x{Hq}x{Hkv}x{d}", t, p)
 
@@ -170,6 +169,7 @@ def paged_decode(B, Hq, Hkv, d, dtype, seed, page_size, lo=1024, hi=32768, chunk
     return Workload(f"paged_decode_{dtype}_{B}x{Hq}x{Hkv}x{d}_P{page_size}", t, p)
 
 
+# The five workloads the library is measured on, with their sizes.
 CONFIGS = {
     "c1_fp16_fwd_small": lambda: prefill(1, 4, 4, 128, 128, 64, "f16", seed=1),
     "c2_fp16_fwd": lambda: prefill(1, 8, 8, 4096, 4096, 64, "f16", seed=2),

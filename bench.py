@@ -132,6 +132,41 @@ def bench_decode(name, w, steps, warmup, torch, eta):
             "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
 
 
+def bench_decode_paged(name, w, steps, warmup, torch, eta):
+    t, p = w.tensors, w.params
+    q, kp, vp = (t[n].cuda() for n in ("q", "k_pages", "v_pages"))
+    bt, lens = t["block_table"].cuda(), t["seqlens"].cuda()
+    ws = torch.empty(eta.decode_workspace_size(p["B"], p["Hq"], p["max_pages"] * p["page_size"], p["d"],
+                                               p["chunk"]), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((p["B"], p["Hq"], 1), dtype=torch.float32, device="cuda")
+    fn = lambda: eta.attn_decode_paged(q, kp, vp, bt, lens, scale=p["scale"], chunk=p["chunk"], workspace=ws,
+                                       o=o, lse=lse)
+    per, region = _time_launches(fn, steps, warmup, torch)
+    total_keys = int(t["seqlens"].sum())
+    kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
+    med = region / steps
+    return {"workload": name, "kernel": "paged decode split + merge", "ms_median": med,
+            "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
+            "page_size": p["page_size"], "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
+
+
+def bench_fwd_varlen(name, w, steps, warmup, torch, eta):
+    t, p = w.tensors, w.params
+    q, k, v, cq, ck = (t[n].cuda() for n in ("q", "k", "v", "cu_q", "cu_k"))
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
+    fn = lambda: eta.attn_fwd_varlen(q, k, v, cq, ck, p["max_seqlen_q"], p["max_seqlen_k"], scale=p["scale"],
+                                     causal=p["causal"], o=o, lse=lse)
+    per, region = _time_launches(fn, steps, warmup, torch)
+    sq, sk = p["seqlens_q"], p["seqlens_k"]
+    flops = sum(_fwd_flops(1, p["Hq"], a, b, p["d"], p["causal"]) for a, b in zip(sq, sk))
+    med = region / steps
+    return {"workload": name, "kernel": "fwd_kernel (packed)", "ms_median": med,
+            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
+            "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}
+
+
 def bench_fp8(name, w, steps, warmup, torch, eta):
     t, p = w.tensors, w.params
     q8, k8, v8 = (t[n].cuda() for n in ("q8", "k8", "v8"))
@@ -224,6 +259,17 @@ def main():
                 configs["c3_bwd"] = {"error": str(e)}
             del bufs, w3
             torch.cuda.empty_cache()
+            _log("[bench] c3 packed variable-length prefill fwd")
+            lens = attn_inputs.decode_lengths(3, 8, 256, 4096).tolist()
+            w3v = attn_inputs.varlen_prefill(lens, lens, 32, 8, 128, "bf16", seed=3, causal=True)
+            try:
+                configs["c3_fwd_varlen"] = bench_fwd_varlen(
+                    f"bf16 causal GQA packed Hq=32 Hkv=8 d=128, 8 sequences S~U[256,4096] (total {sum(lens)})",
+                    w3v, max(5, args.steps // 3), 2, torch, eta)
+            except eta.AttnError as e:
+                configs["c3_fwd_varlen"] = {"error": str(e)}
+            del w3v
+            torch.cuda.empty_cache()
         if "c4" in want:
             _log("[bench] c4 split-KV decode")
             w4 = attn_inputs.CONFIGS["c4_bf16_decode"]()
@@ -233,6 +279,16 @@ def main():
             except eta.AttnError as e:
                 configs["c4_decode"] = {"error": str(e)}
             del w4
+            torch.cuda.empty_cache()
+            _log("[bench] c4 paged split-KV decode")
+            w4p = attn_inputs.paged_decode(64, 32, 8, 128, "bf16", seed=4, page_size=128)
+            try:
+                configs["c4_decode_paged"] = bench_decode_paged(
+                    "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768] chunk 256, paged pool P=128, "
+                    "permuted block table", w4p, args.steps, args.warmup, torch, eta)
+            except eta.AttnError as e:
+                configs["c4_decode_paged"] = {"error": str(e)}
+            del w4p
             torch.cuda.empty_cache()
         if "c5" in want:
             _log("[bench] c5 fp8 forward")

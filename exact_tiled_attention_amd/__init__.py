@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -157,4 +157,34 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=256, wor
                                    B, Hq, Hkv, Smax, d, scale, chunk, _code(q.dtype), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("attn_decode_splitkv", st)
+    return o, lse
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, chunk=256, workspace=None,
+                      o=None, lse=None, stream=None):
+    """Split-KV decode over a paged pool: q [B,Hq,1,d], pools [num_pages,Hkv,P,d],
+    block_table int32 [B, max_pages], seqlens int32 [B], all on the device."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _require(t, n, 4)
+    _require(block_table, "block_table", 2)
+    B, Hq, _, d = q.shape
+    num_pages, Hkv, P = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_pages = block_table.shape[1]
+    _expect(q, "q", (B, Hq, 1, d), q.dtype, q.device)
+    _expect(k_pages, "k_pages", (num_pages, Hkv, P, d), q.dtype, q.device)
+    _expect(v_pages, "v_pages", (num_pages, Hkv, P, d), q.dtype, q.device)
+    _expect(block_table, "block_table", (B, max_pages), torch.int32, q.device)
+    _expect(seqlens, "seqlens", (B,), torch.int32, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, 1), torch.float32, q.device)
+    need = decode_workspace_size(B, Hq, max_pages * P, d, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens), _ptr(o),
+                                 _ptr(lse), B, Hq, Hkv, num_pages, P, max_pages, d, scale, chunk, _code(q.dtype),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("attn_decode_paged", st)
     return o, lse

@@ -215,4 +215,41 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   return hip_status(attn_launch_decode(a, (hipStream_t)stream));
 }
 
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int* block_table, const int* seqlens_k, void* o, float* lse,
+                      int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                      float scale, int chunk, attn_dtype_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k_pages == nullptr || v_pages == nullptr || block_table == nullptr ||
+      seqlens_k == nullptr || o == nullptr)
+    return ATTN_ERR_NULL;
+  if (page_size < 64 || page_size > 4096 || (page_size & (page_size - 1)) != 0) return ATTN_ERR_ARG;
+  if (num_pages <= 0 || max_pages <= 0 || (int64_t)max_pages * page_size > kMaxSeq) return ATTN_ERR_SHAPE;
+  const int Smax = max_pages * page_size;
+  int st = check_dims(B, Hq, Hkv, 1, Smax, d, false);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (chunk <= 0 || chunk % 64 != 0 || chunk > 4096 || !isfinite(scale)) return ATTN_ERR_ARG;
+  if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;
+  const size_t need = attn_decode_workspace_size(B, Hq, Smax, d, chunk);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  DecodeArgs a = {};
+  a.q = q; a.k = k_pages; a.v = v_pages; a.seqlens = seqlens_k; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Smax = Smax; a.d = d; a.chunk = chunk;
+  a.nchunk = decode_chunks(Smax, chunk);
+  const size_t parts = (size_t)B * Hq * a.nchunk;
+  a.part_ml = (float*)workspace;
+  a.part_u = (float*)((char*)workspace + align256(parts * 2 * sizeof(float)));
+  a.group = Hq / Hkv;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  a.page_shift = sh;
+  return hip_status(attn_launch_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

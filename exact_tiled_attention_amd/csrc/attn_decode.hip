@@ -59,7 +59,10 @@ template <> struct Mfma16<bf16> {
 template <int D> __device__ inline int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D> __device__ inline int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
-template <typename T, int D, int G>
+// PG: K/V come from a paged pool [num_pages, Hkv, P, D] through the block table
+// (logical page i of sequence b is physical page block_table[b, i]); otherwise from
+// contiguous caches [B, Hkv, Smax, D].
+template <typename T, int D, int G, bool PG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int DC = D / 32;          // contraction chunks of the score product
   constexpr int DB = D / 16;          // 16-wide d blocks of the output
@@ -80,23 +83,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int kvh = bkv - b * a.Hkv;
   const int h0 = kvh * a.group + blockIdx.z * G;   // first query head of this pass
 
-  int len = a.seqlens[b];
-  len = len < 0 ? 0 : (len > a.Smax ? a.Smax : len);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int kbeg = c * a.chunk;
+
+  // Paged: physical page of the logical page holding key x (the table index clamped
+  // into the row, the entry into the pool: a bad entry reads wrong rows, in bounds).
+  // The wave's first lookup is issued before the length is known, so that the two
+  // loads overlap; each later one is issued a pass ahead.
+  auto page_of = [&](int x) {
+    const int lp = min(x >> a.page_shift, a.max_pages - 1);
+    return min(max(a.block_table[(int64_t)b * a.max_pages + lp], 0), a.num_pages - 1);
+  };
+  int pg_next = 0;
+  if constexpr (PG) pg_next = page_of(kbeg + kSub * w);
+  int len = a.seqlens[b];
+  if constexpr (PG) asm volatile("" : : "s"(pg_next), "s"(len));   // both lookups before the length test
+  len = len < 0 ? 0 : (len > a.Smax ? a.Smax : len);
   if (kbeg >= len) return;                          // whole workgroup: no barrier reached
   const int kend = min(kbeg + a.chunk, len);
 
-  const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  const T* kbase = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Smax) * D;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Smax) * D;
   // loads past the sequence's length return zero (the buffer range check)
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)len * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)len * D * 2);
+  const int64_t head_row0 = PG ? 0 : (int64_t)(b * a.Hkv + kvh) * a.Smax;
+  const T* kbase = reinterpret_cast<const T*>(a.k) + head_row0 * D;
+  const T* vbase = reinterpret_cast<const T*>(a.v) + head_row0 * D;
+  __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)len * D * 2);
+  __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)len * D * 2);
   const T* qbase = reinterpret_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h0) * D;
   uint8_t* vt = s_v[w];
 
@@ -119,16 +135,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // All of the pass's loads first, each wave-wide load 1 KiB of whole rows with the
     // streaming hint (every byte is read once); K then V go through the wave's LDS
     // region, K first.
+    // Paged: the pass's 64 keys lie in one page (P is a power of two >= 64 and base a
+    // multiple of 64); its rows of this head are contiguous.  The resource covers the
+    // page rows below the sequence length, so rows past it read as zero as above.
+    int row0 = base;
+    if constexpr (PG) {
+      const int pg = pg_next;
+      const int in_page = base & ((1 << a.page_shift) - 1);
+      const int64_t prow = ((int64_t)pg * a.Hkv + kvh) * (1 << a.page_shift) + in_page;
+      const uint32_t bytes = (uint32_t)min(kSub, len - base) * D * 2;
+      kr = make_rsrc(reinterpret_cast<const T*>(a.k) + prow * D, bytes);
+      vr = make_rsrc(reinterpret_cast<const T*>(a.v) + prow * D, bytes);
+      row0 = 0;
+    }
     u32x4 kv[VLD], vv[VLD];
 #pragma unroll
     for (int r = 0; r < VLD; ++r) {
       const int idx = r * 64 + lane;
-      kv[r] = buf_load_16_stream(kr, (uint32_t)((base + idx / CPR) * D + 8 * (idx % CPR)) * 2);
+      kv[r] = buf_load_16_stream(kr, (uint32_t)((row0 + idx / CPR) * D + 8 * (idx % CPR)) * 2);
     }
 #pragma unroll
     for (int r = 0; r < VLD; ++r) {
       const int idx = r * 64 + lane;
-      vv[r] = buf_load_16_stream(vr, (uint32_t)((base + idx / CPR) * D + 8 * (idx % CPR)) * 2);
+      vv[r] = buf_load_16_stream(vr, (uint32_t)((row0 + idx / CPR) * D + 8 * (idx % CPR)) * 2);
+    }
+    if constexpr (PG) {
+      if (base + 4 * kSub < kend) pg_next = page_of(base + 4 * kSub);
     }
 #pragma unroll
     for (int r = 0; r < VLD; ++r) {
@@ -316,7 +348,10 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D, int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.nchunk, (unsigned)(a.B * a.Hkv), (unsigned)(a.group / G));
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), grid, dim3(kThreads), 0, stream, a);
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, true>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, false>), grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2((unsigned)((a.B * a.Hq + 3) / 4));

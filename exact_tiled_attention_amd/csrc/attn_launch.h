@@ -76,6 +76,10 @@ struct DecodeArgs {
   int group;
   int dtype_bf16;
   float scale_log2;
+  // paged pool (block_table != nullptr): k, v [num_pages, Hkv, 1 << page_shift, d];
+  // block_table [B, max_pages]; Smax = max_pages << page_shift
+  const int* block_table;
+  int max_pages, num_pages, page_shift;
 };
 
 hipError_t attn_launch_fwd(const FwdArgs& a, hipStream_t stream);

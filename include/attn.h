@@ -180,6 +180,32 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         void* stream);
 
 /*
+ * attn_decode_paged -- attn_decode_splitkv over a paged K/V pool.
+ * "M4.6 - FlashAttention-3/4 Hardware Pipelines ...", section 0x03 (a paged source
+ * supplies a logical K/V block from a physical page named by a page index; masking a
+ * tail score does not by itself make the page read safe), with the split and merge of
+ * attn_decode_splitkv ("M4.4 - FlashAttention-2 ...", section 0x00A defers paged-cache
+ * addressing of split-KV decode to a later article, so its layout here is this
+ * library's reading).  Key j of sequence b is row j % P of page block_table[b, j / P].
+ *
+ *   q [B,Hq,1,d]; k_pages, v_pages [num_pages, Hkv, P, d]: element type `dtype`  (in)
+ *   block_table: device int32 [B, max_pages]; entries in [0, num_pages); only the
+ *       first ceil(seqlens_k[b] / P) entries of row b are read; an entry outside
+ *       the pool is clamped into it (wrong rows, never an access outside the pool) (in)
+ *   seqlens_k: device int32 [B], clamped to [0, max_pages * P]                   (in)
+ *   page_size P: a power of two, 64 <= P <= 4096 (else ATTN_ERR_ARG); rows of a page
+ *       past the sequence length are never read (they may hold anything).
+ *   o [B,Hq,1,d] element type `dtype`; lse [B,Hq,1] float32 (may be NULL)        (out)
+ *   chunk: as for attn_decode_splitkv.
+ *   workspace: >= attn_decode_workspace_size(B, Hq, max_pages * P, d, chunk) bytes
+ */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int* block_table, const int* seqlens_k, void* o, float* lse,
+                      int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                      float scale, int chunk, attn_dtype_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
  * attn_tile_plan -- host-side view of the causal / tail tile iterator the kernels use.
  * For query rows [q_begin, q_end) against S_k keys in tiles of `block_k`, writes the
  * number of key tiles visited in ascending order (*n_visit) and the index of the

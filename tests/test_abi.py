@@ -68,7 +68,7 @@ def test_fwd_varlen_argument_checks():
                  a["d"], scale, 1, dtype, None)
     assert call(cuq=None) == -1 and call(cuk=None) == -1 and call(q=None) == -1 and call(k=None) == -1
     assert call(B=0) == -2 and call(mq=-1) == -2 and call(tk=-1) == -2 and call(mq=1 << 21) == -2
-    assert call(Hq=64, mq=1 << 20) == -2                       # one sequence spans >= 4 GiB
+    assert call(Hq=64, mq=1 << 20) == -2                       # one sequence spans >= 2 GiB
     assert call(Hq=3) == -3 and call(d=80) == -4 and call(dtype=2) == -5
     assert call(scale=float("nan")) == -8
     # nothing to compute: no launch, no dereference of the placeholders
@@ -110,6 +110,23 @@ def test_decode_and_fp8_checks():
         return lib.attn_fwd_fp8(P, P, P, P, P, P, P, None, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], d,
                                 0.088, causal, odt, None)
     assert f8(d=64) == -4 and f8(causal=1) == -8 and f8(odt=0) == -5 and f8(Sk=0) == -2
+
+
+def test_decode_paged_argument_checks():
+    lib, _ = _lib()
+    ws = lib.attn_decode_workspace_size(2, 8, 4 * 128, 128, 256)
+    def call(q=P, bt=P, lens=P, P_=128, maxp=4, npages=9, chunk=256, ws_bytes=ws, **kw):
+        a = dict(B=2, Hq=8, Hkv=2, d=128, dtype=1)
+        a.update(kw)
+        return lib.attn_decode_paged(q, P, P, bt, lens, P, None, a["B"], a["Hq"], a["Hkv"], npages, P_, maxp,
+                                     a["d"], 0.088, chunk, a["dtype"], P, ws_bytes, None)
+    assert call(q=None) == -1 and call(bt=None) == -1 and call(lens=None) == -1
+    assert call(P_=32) == -8 and call(P_=96) == -8 and call(P_=8192) == -8     # power of two, 64 .. 4096
+    assert call(npages=0) == -2 and call(maxp=0) == -2 and call(maxp=1 << 14, P_=128) == -2
+    assert call(Hkv=3) == -3 and call(d=80) == -4 and call(dtype=2) == -5
+    assert call(chunk=100) == -8 and call(ws_bytes=ws - 1) == -6
+    # the workspace is sized for max_pages * P keys
+    assert call(maxp=8, ws_bytes=ws) == -6
 
 
 def test_tile_plan_matches_printed_causal_ledger():
