@@ -96,5 +96,32 @@ __device__ inline u32x2 buf_load_8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) 
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));
 }
 
+// 32-bit LDS byte address of a pointer into __shared__ memory.
+__device__ inline uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address dst + 16 l (dst wave-uniform); out-of-range lanes write zeros.  Issued as an
+// asm statement so that the compiler does not add its own (full) vmcnt waits before
+// LDS reads of the ring: the kernels wait explicitly with wait_vmcnt.  The statement
+// sets M0, which the kernels' compiled code does not otherwise use.
+__device__ inline void lds_load_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t dst) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(dst)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N); the other counters are not waited on).
+template <int N> __device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // True in every lane when the predicate holds in at least one active lane.
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }

@@ -57,6 +57,8 @@
 #include "attn_launch.h"
 #include "tile_plan.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int kWave = 64;
@@ -103,7 +105,9 @@ void fwd_kernel(FwdArgs a) {
   constexpr int DB = D / 32;                  // output d blocks of 32
   constexpr int PC = BC / 16;                 // key chunks of 16 for P V
   constexpr int KPC = KC / PC;                // score contraction chunks per key chunk
-  constexpr int RING = 4 * TL::BYTES;         // K slots 0, 1 then V slots 0, 1
+  // K/V ring depth: three slots each where the key ranges' rings fit the LDS, else two.
+  constexpr int DEPTH = KS * 6 * TL::BYTES <= 160 * 1024 ? 3 : 2;
+  constexpr int RING = 2 * DEPTH * TL::BYTES; // K slots then V slots
   constexpr int NTK = RW * kWave;             // threads staging one key range
   constexpr int LOADS = TL::CHUNKS / NTK;     // 16-byte K (and V) chunks per thread
   static_assert(TL::CHUNKS % NTK == 0 && LOADS >= 1, "chunks must split evenly over the threads");
@@ -122,7 +126,7 @@ void fwd_kernel(FwdArgs a) {
   const int grp = lane >> 5;
   const int tid = threadIdx.x % NTK;          // index among the threads of this key range
   uint8_t* kring = lds_all + kh * RING;
-  uint8_t* vring = kring + 2 * TL::BYTES;
+  uint8_t* vring = kring + DEPTH * TL::BYTES;
 
   const int BH = a.B * a.Hq;
   const int wg = blockIdx.x;
@@ -207,43 +211,39 @@ void fwd_kernel(FwdArgs a) {
   }
 
   // Staging: chunk idx = r * NTK + tid of a tile is LDS (row, pos) = (idx / CPR,
-  // idx % CPR) and holds global chunk pos ^ swz(row) of that row.  Load round r covers
-  // rows r*RS .. r*RS+RS-1 and the swizzles repeat every 16 rows, so a thread's
-  // column offset is the same in every round.  Padded layout: one resource over the
-  // head's rows, the row offsets are compile-time multiples of D.  Packed layout
-  // (runtime row stride): a per-round resource (uniform base and remaining range)
-  // with one shared vector offset, which keeps the stride products out of VGPRs.
+  // idx % CPR) and holds global chunk pos ^ swz(row) of that row.  The loads go
+  // straight from HBM/L2 to LDS (a wave's 64 lanes fill 1 KiB at consecutive 16-byte
+  // positions), so staging takes no registers and no LDS writes; each thread waits for
+  // its own loads (vmcnt) and the step's barrier publishes them.  Load round r covers
+  // rows r*RS .. r*RS+RS-1 and the swizzles repeat every 16 rows, so a thread's column
+  // offset is the same in every round.  Padded layout: one resource over the head's
+  // rows, compile-time row offsets.  Packed layout (runtime row stride): a per-round
+  // resource (uniform base and remaining range) with one shared vector offset.
   constexpr int RS = NTK / TL::CPR;
   static_assert(RS % 16 == 0 && NTK % TL::CPR == 0, "load rounds must cover whole swizzle periods");
-  u32x4 kreg[LOADS], vreg[LOADS];
   const int trow = tid / TL::CPR, tpos = tid % TL::CPR;
   const uint32_t co_k = (uint32_t)((tpos ^ TL::swz_k(trow)) * 16);
   const uint32_t co_v = (uint32_t)((tpos ^ TL::swz_v(trow)) * 16);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)kv_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)kv_bytes);
-  auto load_tile = [&](u32x4 (&dst)[LOADS], const T* src, int t, bool is_v) {
+  const int wsub = tid / kWave;               // wave within this key range's group
+  auto load_tile = [&](uint8_t* ring, int slot, const T* src, int t, bool is_v) {
     const uint32_t co = is_v ? co_v : co_k;
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds_offset(ring + slot * TL::BYTES + (r * NTK + wsub * kWave) * 16));
       if constexpr (VL) {
-        const int64_t off = (int64_t)(t * BC + r * RS) * kv_rs * 2;
+        // the resource must be uniform (SGPRs): t is, but not provably so
+        const int64_t off = (int64_t)(__builtin_amdgcn_readfirstlane(t) * BC + r * RS) * kv_rs * 2;
         const uint32_t left = kv_bytes > off ? (uint32_t)(kv_bytes - off) : 0u;
-        dst[r] = buf_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(src) + off, left),
-                             (uint32_t)(trow * kv_rs * 2) + co);
+        lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(src) + off, left),
+                    (uint32_t)(trow * kv_rs * 2) + co, dst);
       } else {
-        dst[r] = buf_load_16(is_v ? vr : kr, (uint32_t)((t * BC + r * RS + trow) * D * 2) + co);
+        lds_load_16(is_v ? vr : kr, (uint32_t)((t * BC + r * RS + trow) * D * 2) + co, dst);
       }
     }
   };
-  auto store_tile = [&](const u32x4 (&src)[LOADS], uint8_t* slot_base) {
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) st_lds_16(slot_base + (r * NTK + tid) * 16, src[r]);
-  };
-  auto load_k = [&](int t) { load_tile(kreg, kb, t, false); };
-  auto load_v = [&](int t) { load_tile(vreg, vb, t, true); };
-  auto store_k = [&](int slot) { store_tile(kreg, kring + slot * TL::BYTES); };
-  auto store_v = [&](int slot) { store_tile(vreg, vring + slot * TL::BYTES); };
-
   // S^T MFMAs for contraction chunks [kc0, kc1) of one tile from K slot `slot`, each K
   // fragment shared by the QB query blocks; chunk kc = 0 starts from zero.
   auto score_part = [&](f32x16 (&sc)[QB][KB], int slot, int kc0, int kc1) {
@@ -308,29 +308,41 @@ void fwd_kernel(FwdArgs a) {
 
   // Row max of tile t and the rescale decision (one per wave, over its QB blocks); l
   // is rescaled here, O by the caller (after the pending P V product).
-  auto row_max = [&](f32x16 (&sc)[QB][KB], int t, float (&alpha)[QB]) -> bool {
+  // MASK (a compile-time tag): the tile may hold invisible keys; the unmasked form
+  // carries no mask code at all.
+  auto row_max = [&](auto mask_tag, f32x16 (&sc)[QB][KB], int t, float (&alpha)[QB]) -> bool {
+    constexpr bool MASK = decltype(mask_tag)::value;
     float mx[QB];
     bool up = false;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
-      if (t >= wplan.first_masked) {
+      if (MASK && t >= wplan.first_masked) {
+        // key offset within the tile against this lane's limit: the per-register
+        // offsets are constants, so the test is one compare per register
+        const int lim = klim[j] - t * BC - 4 * grp;
 #pragma unroll
         for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
-            sc[j][kbk][i] = key < klim[j] ? sc[j][kbk][i] : -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            sc[j][kbk][i] = (kbk * 32 + 8 * (i >> 2) + (i & 3)) < lim ? sc[j][kbk][i] : -INFINITY;
       }
-      float r0 = vmax(sc[j][0][0], sc[j][0][1]), r1 = vmax(sc[j][0][2], sc[j][0][3]);
+      // two chains of three-input maxima: 8 instructions per 16 values
+      const f32x16& v = sc[j][0];
+      float r0 = vmax(vmax(v[0], v[1]), v[2]), r1 = vmax(vmax(v[8], v[9]), v[10]);
+      r0 = vmax(vmax(r0, v[3]), v[4]);
+      r1 = vmax(vmax(r1, v[11]), v[12]);
+      r0 = vmax(vmax(r0, v[5]), v[6]);
+      r1 = vmax(vmax(r1, v[13]), v[14]);
 #pragma unroll
-      for (int kbk = 0; kbk < KB; ++kbk)
+      for (int kbk = 1; kbk < KB; ++kbk) {
+        const f32x16& u = sc[j][kbk];
 #pragma unroll
-        for (int i = (kbk == 0 ? 4 : 0); i < 16; i += 4) {
-          r0 = vmax(r0, vmax(sc[j][kbk][i], sc[j][kbk][i + 1]));
-          r1 = vmax(r1, vmax(sc[j][kbk][i + 2], sc[j][kbk][i + 3]));
+        for (int i = 0; i < 8; i += 2) {
+          r0 = vmax(vmax(r0, u[i]), u[i + 1]);
+          r1 = vmax(vmax(r1, u[8 + i]), u[8 + i + 1]);
         }
-      mx[j] = max_pair32(vmax(r0, r1) * c);
+      }
+      mx[j] = max_pair32(vmax(vmax(r0, r1), vmax(v[7], v[15])) * c);
       up = up || (mx[j] > m_i[j] + kTau);
     }
     const bool moved = wave_any(up);
@@ -365,42 +377,47 @@ void fwd_kernel(FwdArgs a) {
   const int we = max(tb, min(te, wplan.n_visit));
   const int nr = te - tb;
 
-  // Prologue: K(tb), V(tb), K(tb+1) into LDS; V(tb+1), K(tb+2) into the staging
-  // registers.  All five loads are issued before the first LDS write waits.
-  {
-    u32x4 k0[LOADS], v0[LOADS], k1[LOADS];
-    if (nr > 0) {
-      load_tile(k0, kb, tb, false);
-      load_tile(v0, vb, tb, true);
-    }
-    if (nr > 1) {
-      load_tile(k1, kb, tb + 1, false);
-      load_v(tb + 1);
-    }
-    if (nr > 2) load_k(tb + 2);
-    if (nr > 0) {
-      store_tile(k0, kring);
-      store_tile(v0, vring);
-    }
-    if (nr > 1) store_tile(k1, kring + TL::BYTES);
+  // Relative tile i (absolute tb + i) lives in slot i % DEPTH of its ring.  Step i
+  // reads K(i+1) and V(i) and loads K(i+DEPTH) and V(i+DEPTH-1), into the slots that
+  // K(i) and V(i-1) held until step i-1.
+  auto load_k = [&](int i) { load_tile(kring, i % DEPTH, kb, tb + i, false); };
+  auto load_v = [&](int i) { load_tile(vring, i % DEPTH, vb, tb + i, true); };
+  // Prologue: K0 V0 K1 (then V1 K2 with three slots); K0 is needed first.
+  if (nr > 0) {
+    load_k(0);
+    load_v(0);
   }
+  if (nr > 1) load_k(1);
+  if constexpr (DEPTH == 3) {
+    if (nr > 1) load_v(1);
+    if (nr > 2) load_k(2);
+  }
+  if (nr >= DEPTH)
+    wait_vmcnt<(2 * DEPTH - 2) * LOADS>();   // the loads issued after K0 may stay in flight
+  else
+    wait_vmcnt<0>();
   __syncthreads();
   f32x16 sa[QB][KB], sb[QB][KB];
   if (tb < we) {
     score_part(sa, 0, 0, KC);
     float alpha[QB];
-    row_max(sa, tb, alpha);   // O is still zero: no rescale needed
+    row_max(std::true_type{}, sa, tb, alpha);   // O is still zero: no rescale needed
   }
 
   // One step: tile t = tb + i is in `cur` (scored, its max taken); tile t+1 is scored
   // into `nxt`.
-  auto step = [&](int i, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
+  auto step = [&](auto mask_tag, int i, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
     const int t = tb + i;
-    __syncthreads();   // writes of the step before are visible; the slots written below are free
-    if (t + 2 < te) store_k(i & 1);
-    if (t + 1 < te) store_v((i + 1) & 1);
-    if (t + 3 < te) load_k(t + 3);
-    if (t + 2 < te) load_v(t + 2);
+    // K(i+1) and V(i) must have landed: only the previous step's loads (if it issued
+    // a full set) may still be in flight.  The barrier then publishes every thread's
+    // part and frees the slots loaded below.
+    if (DEPTH == 3 && t + 2 < te)
+      wait_vmcnt<2 * LOADS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (t + DEPTH < te) load_k(i + DEPTH);
+    if (t + DEPTH - 1 < te) load_v(i + DEPTH - 1);
 
     const bool has_cur = t < we;
     const bool has_nxt = t + 1 < we;
@@ -419,33 +436,44 @@ void fwd_kernel(FwdArgs a) {
       // steady state: one basic block, chunk by chunk
 #pragma unroll
       for (int cc = 0; cc < PC; ++cc) {
-        score_part(nxt, (i + 1) & 1, cc * KPC, (cc + 1) * KPC);
+        score_part(nxt, (i + 1) % DEPTH, cc * KPC, (cc + 1) * KPC);
         u32x4 p[QB];
         probs(cc, p);
-        pv_chunk(p, i & 1, cc);
+        pv_chunk(p, i % DEPTH, cc);
       }
     } else if (has_cur) {
 #pragma unroll
       for (int cc = 0; cc < PC; ++cc) {
         u32x4 p[QB];
         probs(cc, p);
-        pv_chunk(p, i & 1, cc);
+        pv_chunk(p, i % DEPTH, cc);
       }
     } else if (has_nxt) {
-      score_part(nxt, (i + 1) & 1, 0, KC);
+      score_part(nxt, (i + 1) % DEPTH, 0, KC);
     }
 #pragma unroll
     for (int j = 0; j < QB; ++j) l_i[j] += l0[j] + l1[j];
     if (has_nxt) {
       float alpha[QB];
-      if (row_max(nxt, t + 1, alpha)) rescale_o(alpha);
+      if (row_max(mask_tag, nxt, t + 1, alpha)) rescale_o(alpha);
     }
   };
+  // Step i takes the row max of tile tb + i + 1: the masked form from the first
+  // masked tile of this wave's rows on.
   for (int i = 0; i < per; i += 2) {
-    step(i, sa, sb);
-    if (i + 1 < per) step(i + 1, sb, sa);
+    if (tb + i + 1 < wplan.first_masked)
+      step(std::false_type{}, i, sa, sb);
+    else
+      step(std::true_type{}, i, sa, sb);
+    if (i + 1 < per) {
+      if (tb + i + 2 < wplan.first_masked)
+        step(std::false_type{}, i + 1, sb, sa);
+      else
+        step(std::true_type{}, i + 1, sb, sa);
+    }
   }
 
+  wait_vmcnt<0>();   // no ring load may still be in flight when the LDS is reused
   if constexpr (KS > 1) {
     // Merge the key ranges' states of each row in one max frame ("M4.3 - IO-Aware
     // Attention ...", section 0x08B): range r hands its (m, l, u) to range 0 through
