@@ -94,21 +94,28 @@ def bench_fwd(name, w, steps, warmup, torch, eta):
             "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}, (q, k, v, o, lse)
 
 
-def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta):
+def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False):
     t, p = w.tensors, w.params
     q, k, v, o, lse = fwd_bufs
     do = t["do"].cuda()
-    ws = torch.empty(eta.bwd_workspace_size(p["B"], p["Hq"], p["Hkv"], p["Sq"], p["Sk"], p["d"]),
-                     dtype=torch.uint8, device="cuda")
+    if deterministic:
+        nbytes = eta.lib().attn_bwd_deterministic_workspace_size(p["B"], p["Hq"], p["Hkv"], p["Sq"], p["Sk"],
+                                                                 p["d"], 1)
+    else:
+        nbytes = eta.bwd_workspace_size(p["B"], p["Hq"], p["Hkv"], p["Sq"], p["Sk"], p["d"])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"],
-                              grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv)
+                              grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv,
+                              deterministic=deterministic)
     per, region = _time_launches(fn, steps, warmup, torch)
     flops = 2.5 * _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
     med = region / steps
-    return {"workload": name, "kernel": "bwd (preprocess + main + convert)", "ms_median": med,
+    kern = ("bwd deterministic (preprocess + column owner dK/dV + query owner dQ)" if deterministic
+            else "bwd (preprocess + main + convert)")
+    return {"workload": name, "kernel": kern, "ms_median": med,
             "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
             "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}
 
@@ -257,6 +264,12 @@ def main():
                 configs["c3_bwd"] = bench_bwd(name + " bwd", w3, bufs, max(3, args.steps // 5), 1, torch, eta)
             except eta.AttnError as e:
                 configs["c3_bwd"] = {"error": str(e)}
+            try:
+                configs["c3_bwd_deterministic"] = bench_bwd(name + " bwd, deterministic", w3, bufs,
+                                                            max(3, args.steps // 5), 1, torch, eta,
+                                                            deterministic=True)
+            except eta.AttnError as e:
+                configs["c3_bwd_deterministic"] = {"error": str(e)}
             del bufs, w3
             torch.cuda.empty_cache()
             _log("[bench] c3 packed variable-length prefill fwd")

@@ -119,22 +119,44 @@ def bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d) -> int:
 
 
 def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.float32,
-             workspace=None, dq=None, dk=None, dv=None, stream=None):
-    """dQ, dK, dV of attn_fwd (dK/dV already summed over each K/V head's query group)."""
+             workspace=None, dq=None, dk=None, dv=None, stream=None, deterministic=False, dq_splits=1):
+    """dQ, dK, dV of attn_fwd (dK/dV already summed over each K/V head's query group).
+    deterministic=True: no atomics, bitwise-repeatable results; dQ from a query-row owner
+    over dq_splits (1, 2, 4, 8, 16) key ranges whose partials are summed in a fixed tree."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _require(t, n, 4)
     B, Hq, Sq, d = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
+    _expect(k, "k", (B, Hkv, Sk, d), q.dtype, q.device)
+    _expect(v, "v", (B, Hkv, Sk, d), q.dtype, q.device)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(do, "do", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device) if dv is None else dv
-    need = bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
+    _expect(dq, "dq", q.shape, grad_dtype, q.device)
+    _expect(dk, "dk", k.shape, grad_dtype, q.device)
+    _expect(dv, "dv", v.shape, grad_dtype, q.device)
+    if deterministic:
+        need = lib().attn_bwd_deterministic_workspace_size(B, Hq, Hkv, Sq, Sk, d, int(dq_splits))
+    else:
+        need = bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                        _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), _code(q.dtype),
-                        _code(grad_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        _stream(stream))
-    _lib.check("attn_bwd", st)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if deterministic:
+        st = lib().attn_bwd_deterministic(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)),
+                                          _code(q.dtype), _code(grad_dtype), int(dq_splits), _ptr(workspace),
+                                          ws_bytes, _stream(stream))
+        _lib.check("attn_bwd_deterministic", st)
+    else:
+        st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                            _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), _code(q.dtype),
+                            _code(grad_dtype), _ptr(workspace), ws_bytes, _stream(stream))
+        _lib.check("attn_bwd", st)
     return dq, dk, dv
 
 

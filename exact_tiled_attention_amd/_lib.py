@@ -27,6 +27,9 @@ PROTOTYPES = {
     "attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S, _P]),
+    "attn_bwd_deterministic_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_bwd_deterministic": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
+                                    _P, _S, _P]),
     "attn_decode_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),

@@ -63,10 +63,12 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(BwdArgs a) {
       acc += Elem<T>::to_f(__builtin_bit_cast(T, (uint16_t)(x >> 16))) *
              Elem<T>::to_f(__builtin_bit_cast(T, (uint16_t)(y >> 16)));
     }
-    float* dq = a.dq_acc + row * D + 8 * c8;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    st_global_16(dq, z);
-    st_global_16(dq + 4, z);
+    if (a.dq_acc != nullptr) {          // the atomic dQ accumulator (not in deterministic mode)
+      float* dq = a.dq_acc + row * D + 8 * c8;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      st_global_16(dq, z);
+      st_global_16(dq + 4, z);
+    }
   }
   // sum over the LPR lanes of the row (LPR = 8 or 16 consecutive lanes)
 #pragma unroll
@@ -161,7 +163,9 @@ __device__ inline void split_pack4x2(const f32x4& x0, const f32x4& x1, u32x4& hi
   }
 }
 
-template <typename T, typename G, int D, bool CAUSAL>
+// DQ: also add dS K into the float32 dQ accumulator (atomics); without it the kernel
+// produces dK and dV only (deterministic mode computes dQ in bwd_dq_kernel).
+template <typename T, typename G, int D, bool CAUSAL, bool DQ>
 __global__ __launch_bounds__(kNTM) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_main_kernel(BwdArgs a) {
   typedef M16<T> MF;
@@ -350,7 +354,7 @@ void bwd_main_kernel(BwdArgs a) {
     // dS^T -> LDS [key][query]: registers 0..3 of tile t are queries 16t + 4g .. +3.
     uint8_t* dsl = lds + L::DST;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < (DQ ? 2 : 0); ++t) {
       u32x2 pk;
       pk.x = Elem<T>::pack2(dp[t][0], dp[t][1]);
       pk.y = Elem<T>::pack2(dp[t][2], dp[t][3]);
@@ -374,6 +378,7 @@ void bwd_main_kernel(BwdArgs a) {
     else
       compute(std::false_type{}, qt);
     __syncthreads();                                          // (B) dS^T visible
+    if constexpr (DQ)
     // dQ_acc += dS K over the 128 keys: block (query tile tq, d block db) per wave pass;
     // slots = keys 32kc + 4g + i and 32kc + 16 + 4g + i for both operands (A = dS by
     // transpose reads of dS^T, B = K by transpose reads of the K tile); result lane =
@@ -423,6 +428,228 @@ void bwd_main_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// 4. Deterministic dQ: the query-row owner ("M4.4 - FlashAttention-2 ...", section
+// 0x06.1G and its ownership table: with queries as the owner, dQ_i is a direct output).
+// One workgroup owns a 128-row query tile of one (b, h_q) and one of dq_splits
+// contiguous ranges of key tiles; it walks its key tiles in ascending order and keeps
+// dQ in registers, so the summation order is fixed by the grid, not by arrival.  With
+// dq_splits > 1 each range writes a float32 partial and bwd_tree_kernel sums them in
+// a fixed binary tree (the materialised-partials alternative of section 0x06.1F).
+//
+// Layout as in the forward (32x32x16 matrix core, transposed products): a wave owns 32
+// query rows as the N dimension.  Per 64-key tile:
+//   S^T  = K Q^T     (A = K row fragments from LDS, B = Q^T fragments in registers)
+//   dP^T = V dO^T    (A = V row fragments, B = dO^T fragments in registers)
+//   P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)   (per lane: one query)
+//   dQ^T += K^T dS^T (A = K^T by transpose reads of the K tile, B = dS^T in registers:
+//                     the accumulator layout of S^T is already the operand layout).
+// K and V tiles go straight to LDS (two-slot rings, loaded one tile ahead).
+constexpr int kDqRW = 4;                   // waves (32 query rows each) per workgroup
+constexpr int kDqBQ = 32 * kDqRW;
+constexpr int kDqBC = 64;                  // keys per tile
+
+template <typename T, typename G, int D, bool CAUSAL>
+__global__ __launch_bounds__(kDqRW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BwdArgs a) {
+  typedef Elem<T> E;
+  typedef typename E::v8 V8;
+  constexpr int BC = kDqBC;
+  constexpr int KC = D / 16;               // contraction chunks of S^T / dP^T
+  constexpr int KB = BC / 32;              // key blocks of 32
+  constexpr int DB = D / 32;               // d blocks of dQ^T
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int ROWB = D * 2;
+  constexpr int TB = BC * ROWB;            // one tile
+  constexpr int NT = kDqRW * kWave;
+  constexpr int LOADS = BC * CPR / NT;     // 16-byte chunks per thread per tile
+  constexpr int RS = NT / CPR;             // rows per load round
+  static_assert(RS % 16 == 0 && LOADS * NT == BC * CPR, "load rounds cover whole swizzle periods");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * TB];   // K slots 0, 1; V slots 0, 1
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int n = lane & 31;
+  const int grp = lane >> 5;
+
+  const int BH = a.B * a.Hq;
+  const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
+  const int wg = blockIdx.x;
+  const int bh = wg % BH;
+  const int qt = CAUSAL ? (nqt - 1 - wg / BH) : (wg / BH);
+  const int split = blockIdx.y;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int kvh = h / a.group;
+
+  const int q0 = qt * kDqBQ;
+  const int q1 = min(q0 + kDqBQ, a.Sq);
+  const TilePlan plan = plan_rows(q0, q1, a.Sq, a.Sk, BC, CAUSAL);
+  const int ntk = (a.Sk + BC - 1) / BC;
+  const int per = (ntk + a.dq_splits - 1) / a.dq_splits;
+  const int tb = min(plan.n_visit, split * per);
+  const int te = min(plan.n_visit, tb + per);
+
+  // swizzle of the 16-byte chunks of a staged row (16 consecutive rows on distinct
+  // bank groups for the fragment reads)
+  auto swz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+
+  const int64_t rowq0 = (int64_t)(b * a.Hq + h) * a.Sq;
+  const T* qb = reinterpret_cast<const T*>(a.q) + rowq0 * D;
+  const T* dob = reinterpret_cast<const T*>(a.dO) + rowq0 * D;
+  const T* kb = reinterpret_cast<const T*>(a.k) + (int64_t)(b * a.Hkv + kvh) * a.Sk * D;
+  const T* vb = reinterpret_cast<const T*>(a.v) + (int64_t)(b * a.Hkv + kvh) * a.Sk * D;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, (uint32_t)a.Sq * D * 2);
+  const __amdgpu_buffer_rsrc_t dr = make_rsrc(dob, (uint32_t)a.Sq * D * 2);
+
+  // this lane's query row; Q^T and dO^T fragments (column = query, slots d 16kc + 8g)
+  const int qrow = q0 + 32 * w + n;
+  V8 qf[KC], df[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const uint32_t off = (uint32_t)(qrow * D + 16 * kc + 8 * grp) * 2;
+    qf[kc] = as_v8<V8>(buf_load_16(qr, off));
+    df[kc] = as_v8<V8>(buf_load_16(dr, off));
+  }
+  // rows past S_q: P = exp2(-inf) = 0, so they contribute nothing
+  const float lse2 = qrow < a.Sq ? a.lse[rowq0 + qrow] * ATTN_LOG2E : INFINITY;
+  const float dl = qrow < a.Sq ? a.delta[rowq0 + qrow] : 0.f;
+  const int klim = CAUSAL ? min(a.Sk, qrow + (a.Sk - a.Sq) + 1) : a.Sk;
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
+
+  // K / V tile t into slot s: chunk idx = r NT + tid is LDS (row, pos) = (idx / CPR,
+  // idx % CPR) holding global chunk pos ^ swz(row)
+  const int trow = tid / CPR, tpos = tid % CPR;
+  const uint32_t co = (uint32_t)((tpos ^ swz(trow)) * 16);
+  // The tile's and the round's row offsets go into a per-round resource (uniform base,
+  // remaining range), so each thread keeps one vector offset.
+  const int64_t kv_bytes = (int64_t)a.Sk * D * 2;
+  const uint32_t vo = (uint32_t)(trow * ROWB) + co;
+  auto load_tile = [&](int t, int slot) {
+    const int tu = __builtin_amdgcn_readfirstlane(t);
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int64_t off = (int64_t)(tu * BC + r * RS) * ROWB;
+      const uint32_t left = kv_bytes > off ? (uint32_t)(kv_bytes - off) : 0u;
+      const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_offset(lds + slot * TB + (r * NT + w * kWave) * 16));
+      const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_offset(lds + (2 + slot) * TB + (r * NT + w * kWave) * 16));
+      lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(kb) + off, left), vo, kd);
+      lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(vb) + off, left), vo, vd);
+    }
+  };
+
+  const int s16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+  // One key tile, one 32-key block at a time (keeps two score accumulators live).
+  auto step = [&](auto mask_tag, int t, int slot) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const uint8_t* ks = lds + slot * TB;
+    const uint8_t* vs = lds + (2 + slot) * TB;
+#pragma unroll 1
+    for (int kbk = 0; kbk < KB; ++kbk) {
+      f32x16 sc, dp;
+      const int row = kbk * 32 + n;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int off = row * ROWB + (((2 * kc + grp) ^ swz(row)) * 16);
+        const V8 ak = as_v8<V8>(ld_lds_16(ks + off));
+        const V8 av = as_v8<V8>(ld_lds_16(vs + off));
+        sc = E::mfma(ak, qf[kc], kc == 0 ? f32x16{} : sc);
+        dp = E::mfma(av, df[kc], kc == 0 ? f32x16{} : dp);
+        if ((kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+      }
+      // P and dS; register i is key t BC + 32 kbk + 8(i/4) + 4 grp + i%4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(fmaf(sc[i], a.scale_log2, -lse2));
+        if constexpr (MASK) {
+          const int key = t * BC + 32 * kbk + 8 * (i >> 2) + 4 * grp + (i & 3);
+          pv = key < klim ? pv : 0.f;
+        }
+        dp[i] = pv * (dp[i] - dl);
+      }
+      // dQ^T += K^T dS^T, key chunk cc: slots of lane group g = keys 16cc + 8(s/4) + 4g + s%4
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int cc = 2 * kbk + half;
+        const int hb = half * 8;
+        const u32x4 dsp = {E::pack2(dp[hb + 0], dp[hb + 1]), E::pack2(dp[hb + 2], dp[hb + 3]),
+                           E::pack2(dp[hb + 4], dp[hb + 5]), E::pack2(dp[hb + 6], dp[hb + 7])};
+        const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
+        const int r1 = r0 + 8;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int col = 32 * db + dsub;
+          const int ch = col >> 3;
+          const int hf = (col & 7) * 2;
+          const u32x2 lo = tr_read(ks + r0 * ROWB + ((ch ^ swz(r0)) * 16) + hf);
+          const u32x2 hi = tr_read(ks + r1 * ROWB + ((ch ^ swz(r1)) * 16) + hf);
+          dq[db] = E::mfma(as_v8<V8>(u32x4{lo.x, lo.y, hi.x, hi.y}), as_v8<V8>(dsp), dq[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // bound the transpose reads in flight
+      }
+    }
+  };
+
+  if (tb < te) load_tile(tb, 0);
+  for (int t = tb; t < te; ++t) {
+    const int slot = (t - tb) & 1;
+    wait_vmcnt<0>();              // this thread's loads of tile t have landed
+    __syncthreads();              // everyone's have; tile t-1's slot is free
+    if (t + 1 < te) load_tile(t + 1, slot ^ 1);
+    if (t >= plan.first_masked)
+      step(std::true_type{}, t, slot);
+    else
+      step(std::false_type{}, t, slot);
+  }
+
+  // dQ^T registers: lane column = query row, register i = d 32db + 8(i/4) + 4grp + i%4.
+  if (qrow < a.Sq) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dcol = 32 * db + 8 * r4 + 4 * grp;
+        if (a.dq_splits > 1) {
+          float* out = a.dq_part + ((int64_t)split * a.B * a.Hq * a.Sq + rowq0 + qrow) * D + dcol;
+          st_global_16(out, __builtin_bit_cast(u32x4, f32x4{dq[db][4 * r4], dq[db][4 * r4 + 1],
+                                                            dq[db][4 * r4 + 2], dq[db][4 * r4 + 3]}));
+        } else {
+          G* out = reinterpret_cast<G*>(a.dq) + (rowq0 + qrow) * D + dcol;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) store_grad<G>(out + e, dq[db][4 * r4 + e] * a.scale);
+        }
+      }
+  }
+}
+
+// dQ = scale * (fixed binary tree over the dq_splits partials): level by level, the
+// partial 2^l (2m + 1) is added into 2^l (2m).
+template <typename G>
+__global__ __launch_bounds__(kNT) void bwd_tree_kernel(BwdArgs a, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* part = reinterpret_cast<const f32x4*>(a.dq_part);
+  f32x4 v[16];
+  const int np = a.dq_splits;
+#pragma unroll
+  for (int p = 0; p < 16; ++p)
+    if (p < np) v[p] = part[(int64_t)p * n4 + i];
+#pragma unroll
+  for (int st = 1; st < 16; st <<= 1)
+#pragma unroll
+    for (int p = 0; p + st < 16; p += 2 * st)
+      if (p + st < np) v[p] = v[p] + v[p + st];
+  G* out = reinterpret_cast<G*>(a.dq) + 4 * i;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = (G)(v[0][j] * a.scale);
+}
+
 template <typename T, typename G, int D>
 hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
@@ -431,13 +658,31 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.Sk + kBKV - 1) / kBKV), (unsigned)(a.B * a.Hkv));
+  const int64_t n4 = rows * D / 4;
+  if (a.deterministic) {
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, false>), grid, dim3(kNTM), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, false>), grid, dim3(kNTM), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
+    const dim3 gq((unsigned)(nqt * a.B * a.Hq), (unsigned)a.dq_splits);
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.dq_splits == 1) return e;
+    hipLaunchKernelGGL((bwd_tree_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
+    return hipGetLastError();
+  }
   if (a.causal)
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true>), grid, dim3(kNTM), 0, stream, a);
+    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, true>), grid, dim3(kNTM), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false>), grid, dim3(kNTM), 0, stream, a);
+    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, true>), grid, dim3(kNTM), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n4 = rows * D / 4;
   hipLaunchKernelGGL((bwd_convert_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
   return hipGetLastError();
 }

@@ -61,6 +61,12 @@ struct BwdArgs {
   int grad_type;      // attn_dtype_t of dq/dk/dv
   float scale;
   float scale_log2;
+  // deterministic mode: dQ from the query-owner kernel over dq_splits contiguous key
+  // ranges, partials [dq_splits][B,Hq,Sq,d] float32 (when dq_splits > 1) reduced in a
+  // fixed binary tree; no atomics anywhere
+  int deterministic;
+  int dq_splits;
+  float* dq_part;
 };
 
 struct DecodeArgs {

@@ -156,6 +156,31 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_deterministic -- attn_bwd with bitwise-repeatable results (no atomics).
+ * "M4.4 - FlashAttention-2 ...", section 0x06.1F (atomic dQ accumulation has no fixed
+ * order; the alternative materialises one partial per producer and reduces the
+ * partials in a fixed tree) and section 0x06.1G with its ownership table (a query-row
+ * owner makes dQ_i a direct output).  dK and dV come from the column owner as in
+ * attn_bwd (register sums in a fixed order, one write each).  dQ comes from a
+ * query-row owner that recomputes P and dS and walks the key tiles in ascending order:
+ * with dq_splits = 1 it writes dQ directly; with dq_splits = 2, 4, 8 or 16 the key
+ * tiles are cut into that many contiguous ranges, each writes a float32 partial, and
+ * the partials are summed in a fixed binary tree.  The recomputation costs two more
+ * matrix products per tile than attn_bwd's atomic dQ.
+ *
+ *   Arguments as attn_bwd, plus dq_splits (1, 2, 4, 8 or 16; else ATTN_ERR_ARG).
+ *   workspace: >= attn_bwd_deterministic_workspace_size(..., dq_splits) bytes
+ *       (D rows, and the dq_splits partials when dq_splits > 1)             (scratch)
+ */
+size_t attn_bwd_deterministic_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                                             int dq_splits);
+int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                           int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                           attn_dtype_t dtype, attn_dtype_t grad_dtype, int dq_splits,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_splitkv -- one new query per sequence against a K/V cache.
  * "M4.4 - FlashAttention-2 ...", section 0x01 (Flash-Decoding splits the K/V axis
  * into chunks, then reduces over chunks) and "M4.3 - IO-Aware Attention ...",

@@ -150,3 +150,19 @@ def test_tile_plan_matches_printed_causal_ledger():
             assert full == c["full"]
     assert lib.attn_tile_plan(0, 0, 8, 8, 64, 1, ctypes.byref(n), ctypes.byref(fm)) == -8
     assert lib.attn_tile_plan(0, 8, 8, 8, 64, 1, None, ctypes.byref(fm)) == -1
+
+
+def test_bwd_deterministic_argument_checks():
+    lib, _ = _lib()
+    ws1 = lib.attn_bwd_deterministic_workspace_size(1, 4, 2, 8, 8, 64, 1)
+    ws4 = lib.attn_bwd_deterministic_workspace_size(1, 4, 2, 8, 8, 64, 4)
+    assert ws1 >= 1 * 4 * 8 * 4 and ws4 >= ws1 + 4 * 1 * 4 * 8 * 64 * 4
+    assert lib.attn_bwd_deterministic_workspace_size(1, 4, 2, 8, 8, 64, 3) == 0
+    def call(splits=1, ws_bytes=ws1, **kw):
+        a = dict(B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=64)
+        a.update(kw)
+        return lib.attn_bwd_deterministic(P, P, P, P, P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"],
+                                          a["d"], 0.125, 1, 1, 2, splits, P, ws_bytes, None)
+    assert call(splits=3) == -8 and call(splits=32) == -8 and call(splits=0) == -8
+    assert call(splits=4, ws_bytes=ws4 - 1) == -6 and call(ws_bytes=ws1 - 1) == -6
+    assert call(Sk=0) == -2 and call(Hkv=3) == -3 and call(d=32) == -4
