@@ -21,4 +21,6 @@ Modules:
              parity of the quantised output itself is unpinned: no printed values
              exist for this input distribution]
   tiles   -- causal tile classes, visit counts, packed-launch census  [pinned]
+  dropout -- Philox4x32-10 keep decisions by element coordinates, the dropout
+             forward and its backward                              [pinned]
 """
