@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -63,6 +63,28 @@ def attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
     st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                         scale, int(bool(causal)), _code(q.dtype), _stream(stream))
     _lib.check("attn_fwd", st)
+    return o, lse
+
+
+def attn_fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False, o=None, lse=None,
+                     stream=None):
+    """attn_fwd with attention dropout (keep decisions from Philox4x32-10 by element
+    coordinates; LSE of the undropped softmax)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, 4)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    _expect(k, "k", (B, Hkv, Sk, d), q.dtype, q.device)
+    _expect(v, "v", (B, Hkv, Sk, d), q.dtype, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
+    st = lib().attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, scale,
+                                int(bool(causal)), float(dropout_p), int(seed) & (2 ** 64 - 1),
+                                int(offset) & 0xFFFFFFFF, _code(q.dtype), _stream(stream))
+    _lib.check("attn_fwd_dropout", st)
     return o, lse
 
 

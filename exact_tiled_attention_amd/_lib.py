@@ -18,6 +18,8 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _S = ctypes.c_size_t
+_U64 = ctypes.c_ulonglong
+_U32 = ctypes.c_uint
 
 PROTOTYPES = {
     "attn_status_string": (ctypes.c_char_p, [_I]),
@@ -27,6 +29,7 @@ PROTOTYPES = {
     "attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S, _P]),
+    "attn_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _I, _P]),
     "attn_bwd_deterministic_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_bwd_deterministic": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                                     _P, _S, _P]),

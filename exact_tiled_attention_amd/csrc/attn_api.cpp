@@ -79,6 +79,40 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
 }
 
+// Dropout parameters from (p, seed, offset); p must be in [0, 1).
+bool make_drop(float p, unsigned long long seed, unsigned offset, DropParams* dp) {
+  if (!(p >= 0.f && p < 1.f)) return false;
+  const double t = floor((double)p * 4294967296.0);
+  dp->thresh = (uint32_t)(t > 4294967295.0 ? 4294967295.0 : t);
+  dp->seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
+  dp->seed_hi = (uint32_t)(seed >> 32);
+  dp->offset = offset;
+  dp->rp = 1.f / (1.f - p);
+  return true;
+}
+
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     float dropout_p, unsigned long long seed, unsigned offset,
+                     attn_dtype_t dtype, void* stream) {
+  if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (Sk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, true);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  FwdArgs a = {};
+  if (!make_drop(dropout_p, seed, offset, &a.drop)) return ATTN_ERR_ARG;
+  a.dropout = 1;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
+}
+
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                     const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
                     int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int d,

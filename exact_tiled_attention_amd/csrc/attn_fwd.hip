@@ -92,7 +92,9 @@ __device__ inline float max_pair32(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <typename T, int D, int QB, int RW, int KS, bool VL, bool CAUSAL>
+// VL: packed variable-length layout.  DROP: dropout on the probabilities entering P V
+// (padded layout only).
+template <typename T, int D, int QB, int RW, int KS, bool VL, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
@@ -291,17 +293,37 @@ void fwd_kernel(FwdArgs a) {
   // Probabilities of key chunk cc of a scored tile for query block j, packed to the
   // element type (slot s of lane group g = key 16cc + 8(s/4) + 4g + s%4, accumulator
   // registers 8(cc%2) .. +7 of key block cc/2); their fp32 sum goes to l.
-  auto probs_chunk = [&](const f32x16 (&sc)[KB], int cc, float m_use, float& l0, float& l1) -> u32x4 {
+  //
+  // Dropout ("M4.4 - FlashAttention-2 ...", section 0x03I): l sums the undropped
+  // values; the operand of P V carries only the kept ones, and the epilogue scales by
+  // 1 / (1 - p).  Registers 4q .. 4q+3 of a key block are 4 consecutive keys, so one
+  // Philox call (counter (key / 4, query row, b H_q + h, offset)) decides all four.
+  auto probs_chunk = [&](const f32x16 (&sc)[KB], int cc, float m_use, float& l0, float& l1, int t,
+                         int j) -> u32x4 {
     const int kbk = cc >> 1;
     const int hb = (cc & 1) * 8;
+    u32x4 w0 = {}, w1 = {};
+    if constexpr (DROP) {
+      const uint32_t grp4 = (uint32_t)(t * (BC / 4) + kbk * 8 + (hb >> 1) + grp);   // (key of register hb) / 4
+      const uint32_t bhq = (uint32_t)(b * a.Hq + h);
+      w0 = philox4x32_10(grp4, (uint32_t)qrow[j], bhq, a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+      w1 = philox4x32_10(grp4 + 2, (uint32_t)qrow[j], bhq, a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+    }
     uint32_t pk[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e0 = fast_exp2(fmaf(sc[kbk][hb + 2 * j], c, -m_use));
-      const float e1 = fast_exp2(fmaf(sc[kbk][hb + 2 * j + 1], c, -m_use));
+    for (int jj = 0; jj < 4; ++jj) {
+      const float e0 = fast_exp2(fmaf(sc[kbk][hb + 2 * jj], c, -m_use));
+      const float e1 = fast_exp2(fmaf(sc[kbk][hb + 2 * jj + 1], c, -m_use));
       l0 += e0;
       l1 += e1;
-      pk[j] = E::pack2(e0, e1);
+      if constexpr (DROP) {
+        const u32x4& wv = jj < 2 ? w0 : w1;
+        const float k0 = wv[2 * (jj & 1)] >= a.drop.thresh ? e0 : 0.f;
+        const float k1 = wv[2 * (jj & 1) + 1] >= a.drop.thresh ? e1 : 0.f;
+        pk[jj] = E::pack2(k0, k1);
+      } else {
+        pk[jj] = E::pack2(e0, e1);
+      }
     }
     return u32x4{pk[0], pk[1], pk[2], pk[3]};
   };
@@ -430,7 +452,7 @@ void fwd_kernel(FwdArgs a) {
     }
     auto probs = [&](int cc, u32x4 (&p)[QB]) {
 #pragma unroll
-      for (int j = 0; j < QB; ++j) p[j] = probs_chunk(cur[j], cc, m_use[j], l0[j], l1[j]);
+      for (int j = 0; j < QB; ++j) p[j] = probs_chunk(cur[j], cc, m_use[j], l0[j], l1[j], t, j);
     };
     if (has_cur && has_nxt) {
       // steady state: one basic block, chunk by chunk
@@ -521,7 +543,7 @@ void fwd_kernel(FwdArgs a) {
     for (int j = 0; j < QB; ++j) {
       const float l_tot = l_i[j] + __shfl_xor(l_i[j], 32);
       const bool empty = (m_i[j] == -INFINITY) || !(l_tot > 0.f);
-      const float inv = empty ? 0.f : 1.f / l_tot;
+      const float inv = empty ? 0.f : (DROP ? a.drop.rp : 1.f) / l_tot;
       if (qrow[j] < Sq) {
         T* ob = reinterpret_cast<T*>(a.o) + q_off + (int64_t)qrow[j] * q_rs;
 #pragma unroll
@@ -552,14 +574,18 @@ hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   const bool vl = a.cu_q != nullptr;
   if (a.causal) {
     if (vl)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true, false>), grid, block, 0, stream, a);
+    else if (a.dropout)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false>), grid, block, 0, stream, a);
   } else {
     if (vl)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false, false>), grid, block, 0, stream, a);
+    else if (a.dropout)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

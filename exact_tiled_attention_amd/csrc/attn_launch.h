@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn_philox.h"
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -24,6 +26,8 @@ struct FwdArgs {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  int dropout;        // 1: apply dropout with `drop` (padded layout only)
+  DropParams drop;
 };
 
 struct Fp8Args {
@@ -67,6 +71,8 @@ struct BwdArgs {
   int deterministic;
   int dq_splits;
   float* dq_part;
+  int dropout;        // 1: regenerate the forward's dropout decisions from `drop`
+  DropParams drop;
 };
 
 struct DecodeArgs {

@@ -78,6 +78,26 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fwd_dropout -- attn_fwd with attention dropout on the probabilities.
+ * "M4.4 - FlashAttention-2 ...", section 0x03I and "M4.3 - IO-Aware Attention ...",
+ * section 0x0DF: the maximum, the denominator and the LSE stay those of the undropped
+ * softmax; each probability element is kept or dropped before P V and the kept ones
+ * are scaled by 1 / (1 - dropout_p); the decisions are a pure function of the
+ * element's coordinates so attn_bwd_dropout regenerates them.  Element (b, h, query
+ * row i, key j) takes word j % 4 of Philox4x32-10 (counter (j / 4, i, b Hq + h,
+ * offset), key (seed mod 2^32, seed / 2^32)) and is kept iff the word is at least
+ * floor(dropout_p 2^32).
+ *
+ *   Arguments as attn_fwd, plus dropout_p in [0, 1) (else ATTN_ERR_ARG), the 64-bit
+ *   seed and a 32-bit offset (e.g. a step counter: a new offset draws new decisions).
+ */
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     float dropout_p, unsigned long long seed, unsigned offset,
+                     attn_dtype_t dtype, void* stream);
+
+/*
+ * attn_fwd_varlen -- /*
  * attn_fwd_varlen -- the forward of attn_fwd on packed variable-length sequences.
  * "M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary", sections 0x04B
  * (a packed launch covers the longest sequence; workgroups past a sequence's rows
