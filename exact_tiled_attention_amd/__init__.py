@@ -141,10 +141,12 @@ def bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d) -> int:
 
 
 def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.float32,
-             workspace=None, dq=None, dk=None, dv=None, stream=None, deterministic=False, dq_splits=1):
+             workspace=None, dq=None, dk=None, dv=None, stream=None, deterministic=False, dq_splits=1,
+             dropout_p=None, seed=0, offset=0):
     """dQ, dK, dV of attn_fwd (dK/dV already summed over each K/V head's query group).
     deterministic=True: no atomics, bitwise-repeatable results; dQ from a query-row owner
-    over dq_splits (1, 2, 4, 8, 16) key ranges whose partials are summed in a fixed tree."""
+    over dq_splits (1, 2, 4, 8, 16) key ranges whose partials are summed in a fixed tree.
+    dropout_p (with seed, offset): the backward of attn_fwd_dropout with the same values."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _require(t, n, 4)
     B, Hq, Sq, d = q.shape
@@ -168,7 +170,14 @@ def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.flo
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if deterministic:
+    if dropout_p is not None:
+        st = lib().attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), float(dropout_p),
+                                    int(seed) & (2 ** 64 - 1), int(offset) & 0xFFFFFFFF, _code(q.dtype),
+                                    _code(grad_dtype), int(bool(deterministic)), int(dq_splits), _ptr(workspace),
+                                    ws_bytes, _stream(stream))
+        _lib.check("attn_bwd_dropout", st)
+    elif deterministic:
         st = lib().attn_bwd_deterministic(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                                           _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)),
                                           _code(q.dtype), _code(grad_dtype), int(dq_splits), _ptr(workspace),

@@ -260,6 +260,53 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
   return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
 }
 
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     float dropout_p, unsigned long long seed, unsigned offset,
+                     attn_dtype_t dtype, attn_dtype_t grad_dtype, int deterministic, int dq_splits,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+      dO == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, false);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (grad_dtype != ATTN_F32 && grad_dtype != ATTN_BF16 && grad_dtype != ATTN_F16)
+    return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;
+  BwdArgs a = {};
+  if (!make_drop(dropout_p, seed, offset, &a.drop)) return ATTN_ERR_ARG;
+  a.dropout = 1;
+  const size_t rows = (size_t)B * Hq * Sq;
+  if (deterministic) {
+    if (dq_splits < 1 || dq_splits > 16 || (dq_splits & (dq_splits - 1)) != 0) return ATTN_ERR_ARG;
+    const size_t need = attn_bwd_deterministic_workspace_size(B, Hq, Hkv, Sq, Sk, d, dq_splits);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    a.dq_acc = nullptr;
+    a.delta = (float*)workspace;
+    a.dq_part = dq_splits > 1 ? (float*)((char*)workspace + align256(rows * sizeof(float))) : nullptr;
+    a.deterministic = 1;
+    a.dq_splits = dq_splits;
+  } else {
+    const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d);
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    a.dq_acc = (float*)workspace;
+    a.delta = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+  }
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dO = dO;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.grad_type = (int)grad_dtype;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int Smax, int d, int chunk) {
   if (B <= 0 || Hq <= 0 || Smax <= 0 || Smax > kMaxSeq || (int64_t)B * Hq > kMaxBH) return 0;
   if ((d != 64 && d != 128) || chunk <= 0 || chunk % 64 != 0) return 0;

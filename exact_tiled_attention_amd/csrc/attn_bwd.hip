@@ -33,6 +33,7 @@
 #include "../../include/attn.h"
 #include "attn_device.h"
 #include "attn_launch.h"
+#include "attn_philox.h"
 #include "tile_plan.h"
 
 namespace {
@@ -113,7 +114,8 @@ struct BwdLds {
   static constexpr int Q = 0;                 // byte offsets
   static constexpr int DO = Q + BQ * ROWB;
   static constexpr int DST = DO + BQ * ROWB;  // dS^T [key][query], 16-bit, 64-byte rows
-  static constexpr int K = DST + kBKV * BQ * 2;   // K tile, row-major
+  static constexpr int DSL = DST + kBKV * BQ * 2; // its bf16 residual (same layout)
+  static constexpr int K = DSL + kBKV * BQ * 2;   // K tile, row-major
   static constexpr int V = K + kBKV * ROWB;       // V tile, row-major
   static constexpr int BYTES = V + kBKV * ROWB;
 };
@@ -165,7 +167,9 @@ __device__ inline void split_pack4x2(const f32x4& x0, const f32x4& x1, u32x4& hi
 
 // DQ: also add dS K into the float32 dQ accumulator (atomics); without it the kernel
 // produces dK and dV only (deterministic mode computes dQ in bwd_dq_kernel).
-template <typename T, typename G, int D, bool CAUSAL, bool DQ>
+// DROP: regenerate the forward's dropout decisions Z (keep / (1 - p)) and use
+// dV += (P Z)^T dO, dS = P (Z dP - D).
+template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool DROP>
 __global__ __launch_bounds__(kNTM) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_main_kernel(BwdArgs a) {
   typedef M16<T> MF;
@@ -286,7 +290,7 @@ void bwd_main_kernel(BwdArgs a) {
 
   // One step: S / dP for the wave's keys, P and dS, the dV / dK products, dS^T to LDS.
   // MASKED applies the element mask (tails and the causal band).
-  auto compute = [&](auto masked_tag, int qt) {
+  auto compute = [&](auto masked_tag, int qt, int h) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* sq = lds + L::Q;
     const uint8_t* sdo = lds + L::DO;
@@ -325,8 +329,17 @@ void bwd_main_kernel(BwdArgs a) {
           const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
           pv = vis ? pv : 0.f;
         }
-        s[t][i] = pv;
-        dp[t][i] = pv * (dp[t][i] - dl[i]);
+        float z = 1.f;
+        if constexpr (DROP) {
+          // key mykey of query row qr: word mykey % 4 of counter (mykey / 4, qr, b Hq + h, offset)
+          const int qr = qt * BQ + qb + i;
+          const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)qr, (uint32_t)(b * a.Hq + h),
+                                         a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+          const uint32_t word = (mykey & 3) == 0 ? wv[0] : (mykey & 3) == 1 ? wv[1] : (mykey & 3) == 2 ? wv[2] : wv[3];
+          z = word >= a.drop.thresh ? a.drop.rp : 0.f;
+        }
+        s[t][i] = pv * z;
+        dp[t][i] = pv * (z * dp[t][i] - dl[i]);
       }
     }
     // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries 4g + i and
@@ -359,6 +372,14 @@ void bwd_main_kernel(BwdArgs a) {
       pk.x = Elem<T>::pack2(dp[t][0], dp[t][1]);
       pk.y = Elem<T>::pack2(dp[t][2], dp[t][3]);
       st_lds_8(dsl + dst_off(krow, 16 * t + 4 * g), pk);
+      if constexpr (kSplit<T>) {   // bf16: the residual dS - hi enters dQ as well
+        u32x2 lo;
+        lo.x = Elem<T>::pack2(dp[t][0] - __builtin_bit_cast(float, pk.x << 16),
+                              dp[t][1] - __builtin_bit_cast(float, pk.x & 0xFFFF0000u));
+        lo.y = Elem<T>::pack2(dp[t][2] - __builtin_bit_cast(float, pk.y << 16),
+                              dp[t][3] - __builtin_bit_cast(float, pk.y & 0xFFFF0000u));
+        st_lds_8(lds + L::DSL + dst_off(krow, 16 * t + 4 * g), lo);
+      }
     }
   };
 
@@ -374,9 +395,9 @@ void bwd_main_kernel(BwdArgs a) {
 
     const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * BQ > a.Sq;
     if (masked)
-      compute(std::true_type{}, qt);
+      compute(std::true_type{}, qt, h);
     else
-      compute(std::false_type{}, qt);
+      compute(std::false_type{}, qt, h);
     __syncthreads();                                          // (B) dS^T visible
     if constexpr (DQ)
     // dQ_acc += dS K over the 128 keys: block (query tile tq, d block db) per wave pass;
@@ -399,7 +420,13 @@ void bwd_main_kernel(BwdArgs a) {
           const u32x2 ahi = tr_read(dsl + dst_off(kb0 + 16, qcol));
           const u32x2 blo = tr_tile(kt, 32 * kc + 4 * g, 16 * db);
           const u32x2 bhi = tr_tile(kt, 32 * kc + 16 + 4 * g, 16 * db);
-          acc = MF::run(u32x4{alo.x, alo.y, ahi.x, ahi.y}, u32x4{blo.x, blo.y, bhi.x, bhi.y}, acc);
+          const u32x4 kb4 = {blo.x, blo.y, bhi.x, bhi.y};
+          acc = MF::run(u32x4{alo.x, alo.y, ahi.x, ahi.y}, kb4, acc);
+          if constexpr (kSplit<T>) {
+            const u32x2 rlo = tr_read(lds + L::DSL + dst_off(kb0, qcol));
+            const u32x2 rhi = tr_read(lds + L::DSL + dst_off(kb0 + 16, qcol));
+            acc = MF::run(u32x4{rlo.x, rlo.y, rhi.x, rhi.y}, kb4, acc);
+          }
         }
         const int dcol = 16 * db + n;
 #pragma unroll
@@ -449,7 +476,7 @@ constexpr int kDqRW = 4;                   // waves (32 query rows each) per wor
 constexpr int kDqBQ = 32 * kDqRW;
 constexpr int kDqBC = 64;                  // keys per tile
 
-template <typename T, typename G, int D, bool CAUSAL>
+template <typename T, typename G, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kDqRW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(BwdArgs a) {
   typedef Elem<T> E;
@@ -563,23 +590,35 @@ void bwd_dq_kernel(BwdArgs a) {
         dp = E::mfma(av, df[kc], kc == 0 ? f32x16{} : dp);
         if ((kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
       }
-      // P and dS; register i is key t BC + 32 kbk + 8(i/4) + 4 grp + i%4
+      // P and dS; register i is key t BC + 32 kbk + 8(i/4) + 4 grp + i%4, so registers
+      // 4q .. 4q+3 are four consecutive keys: one Philox call decides them (dropout)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(sc[i], a.scale_log2, -lse2));
-        if constexpr (MASK) {
-          const int key = t * BC + 32 * kbk + 8 * (i >> 2) + 4 * grp + (i & 3);
-          pv = key < klim ? pv : 0.f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        u32x4 wv = {};
+        if constexpr (DROP)
+          wv = philox4x32_10((uint32_t)(t * (BC / 4) + 8 * kbk + 2 * q4 + grp), (uint32_t)qrow,
+                             (uint32_t)(b * a.Hq + h), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          float pv = fast_exp2(fmaf(sc[i], a.scale_log2, -lse2));
+          if constexpr (MASK) {
+            const int key = t * BC + 32 * kbk + 8 * (i >> 2) + 4 * grp + (i & 3);
+            pv = key < klim ? pv : 0.f;
+          }
+          const float z = DROP ? (wv[e] >= a.drop.thresh ? a.drop.rp : 0.f) : 1.f;
+          dp[i] = pv * (z * dp[i] - dl);
         }
-        dp[i] = pv * (dp[i] - dl);
       }
       // dQ^T += K^T dS^T, key chunk cc: slots of lane group g = keys 16cc + 8(s/4) + 4g + s%4
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int cc = 2 * kbk + half;
         const int hb = half * 8;
-        const u32x4 dsp = {E::pack2(dp[hb + 0], dp[hb + 1]), E::pack2(dp[hb + 2], dp[hb + 3]),
-                           E::pack2(dp[hb + 4], dp[hb + 5]), E::pack2(dp[hb + 6], dp[hb + 7])};
+        // dS^T operand; bf16 also carries the residual dS - hi (a second product)
+        u32x4 dsp, dsl;
+        split_pack4x2<T>(f32x4{dp[hb + 0], dp[hb + 1], dp[hb + 2], dp[hb + 3]},
+                         f32x4{dp[hb + 4], dp[hb + 5], dp[hb + 6], dp[hb + 7]}, dsp, dsl);
         const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
         const int r1 = r0 + 8;
 #pragma unroll
@@ -589,7 +628,9 @@ void bwd_dq_kernel(BwdArgs a) {
           const int hf = (col & 7) * 2;
           const u32x2 lo = tr_read(ks + r0 * ROWB + ((ch ^ swz(r0)) * 16) + hf);
           const u32x2 hi = tr_read(ks + r1 * ROWB + ((ch ^ swz(r1)) * 16) + hf);
-          dq[db] = E::mfma(as_v8<V8>(u32x4{lo.x, lo.y, hi.x, hi.y}), as_v8<V8>(dsp), dq[db]);
+          const V8 kt8 = as_v8<V8>(u32x4{lo.x, lo.y, hi.x, hi.y});
+          dq[db] = E::mfma(kt8, as_v8<V8>(dsp), dq[db]);
+          if constexpr (kSplit<T>) dq[db] = E::mfma(kt8, as_v8<V8>(dsl), dq[db]);
         }
         __builtin_amdgcn_sched_barrier(0);   // bound the transpose reads in flight
       }
@@ -650,6 +691,15 @@ __global__ __launch_bounds__(kNT) void bwd_tree_kernel(BwdArgs a, int64_t n4) {
   for (int j = 0; j < 4; ++j) out[j] = (G)(v[0][j] * a.scale);
 }
 
+// column-owner launch for one (DQ, DROP) form
+template <typename T, typename G, int D, bool DQ, bool DROP>
+void main_k(const BwdArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.causal)
+    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, DQ, DROP>), grid, dim3(kNTM), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, DQ, DROP>), grid, dim3(kNTM), 0, stream, a);
+}
+
 template <typename T, typename G, int D>
 hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
@@ -660,27 +710,34 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.Sk + kBKV - 1) / kBKV), (unsigned)(a.B * a.Hkv));
   const int64_t n4 = rows * D / 4;
   if (a.deterministic) {
-    if (a.causal)
-      hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, false>), grid, dim3(kNTM), 0, stream, a);
+    if (a.dropout)
+      main_k<T, G, D, false, true>(a, grid, stream);
     else
-      hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, false>), grid, dim3(kNTM), 0, stream, a);
+      main_k<T, G, D, false, false>(a, grid, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
     const dim3 gq((unsigned)(nqt * a.B * a.Hq), (unsigned)a.dq_splits);
-    if (a.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    if (a.dropout) {
+      if (a.causal)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, true, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, false, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    } else {
+      if (a.causal)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, true, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, false, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess || a.dq_splits == 1) return e;
     hipLaunchKernelGGL((bwd_tree_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
     return hipGetLastError();
   }
-  if (a.causal)
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, true>), grid, dim3(kNTM), 0, stream, a);
+  if (a.dropout)
+    main_k<T, G, D, true, true>(a, grid, stream);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, true>), grid, dim3(kNTM), 0, stream, a);
+    main_k<T, G, D, true, false>(a, grid, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_convert_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);

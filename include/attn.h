@@ -201,6 +201,25 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_dropout -- backward of attn_fwd_dropout (same dropout_p, seed and offset).
+ * "M4.4 - FlashAttention-2 ...", section 0x03I (the backward regenerates the forward's
+ * decisions; D = rowsum(dO * O) with the dropped O) and "M4.3 - IO-Aware Attention ...",
+ * section 0x0DF (coordinate-stable replay).  With Z = keep / (1 - p) per element:
+ * dV = (P Z)^T dO, dS = P (Z dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ *
+ *   Arguments as attn_bwd, plus dropout_p, seed, offset as given to attn_fwd_dropout,
+ *   deterministic (0: atomic dQ as attn_bwd, workspace attn_bwd_workspace_size;
+ *   1: as attn_bwd_deterministic with dq_splits, workspace
+ *   attn_bwd_deterministic_workspace_size).
+ */
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     float dropout_p, unsigned long long seed, unsigned offset,
+                     attn_dtype_t dtype, attn_dtype_t grad_dtype, int deterministic, int dq_splits,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_decode_splitkv -- one new query per sequence against a K/V cache.
  * "M4.4 - FlashAttention-2 ...", section 0x01 (Flash-Decoding splits the K/V axis
  * into chunks, then reduces over chunks) and "M4.3 - IO-Aware Attention ...",

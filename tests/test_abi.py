@@ -166,3 +166,18 @@ def test_bwd_deterministic_argument_checks():
     assert call(splits=3) == -8 and call(splits=32) == -8 and call(splits=0) == -8
     assert call(splits=4, ws_bytes=ws4 - 1) == -6 and call(ws_bytes=ws1 - 1) == -6
     assert call(Sk=0) == -2 and call(Hkv=3) == -3 and call(d=32) == -4
+
+
+def test_dropout_argument_checks():
+    lib, _ = _lib()
+    f = lib.attn_fwd_dropout
+    def fwd(p=0.1, **kw):
+        a = dict(B=1, Hq=2, Hkv=2, Sq=8, Sk=8, d=64)
+        a.update(kw)
+        return f(P, P, P, P, None, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], 0.125, 0, p, 1, 0, 1, None)
+    assert fwd(p=1.0) == -8 and fwd(p=-0.1) == -8 and fwd(p=float("nan")) == -8 and fwd(d=80) == -4
+    ws = lib.attn_bwd_workspace_size(1, 2, 2, 8, 8, 64)
+    def bwd(p=0.1, det=0, splits=1, ws_bytes=ws):
+        return lib.attn_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 2, 2, 8, 8, 64, 0.125, 0, p, 1, 0, 1, 2, det,
+                                    splits, P, ws_bytes, None)
+    assert bwd(p=1.0) == -8 and bwd(ws_bytes=ws - 1) == -6 and bwd(det=1, splits=3) == -8

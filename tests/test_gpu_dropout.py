@@ -75,3 +75,53 @@ def test_dropout_zero_rate_is_the_plain_forward_and_repeatable():
     b, lb = eta.attn_fwd_dropout(q, k, v, 0.2, 5, 7, causal=True)
     c, _ = eta.attn_fwd_dropout(q, k, v, 0.2, 5, 8, causal=True)
     assert torch.equal(a, b) and torch.equal(la, l0) and not torch.equal(a, c)
+
+
+def _dropout_grads(w, p, seed, offset, deterministic, dq_splits=1):
+    """Backward from the oracle's dropout forward: O (rounded to the element type, as
+    a forward stores it) and LSE (float32) come from oracle/dropout.py, so the test
+    isolates the backward; both sides form D from the same stored O."""
+    import exact_tiled_attention_amd as eta
+    t, prm = w.tensors, w.params
+    O, L = dropout.forward(t["q"], t["k"], t["v"], prm["scale"], prm["causal"], p, seed, offset)
+    o = to_dev(torch.from_numpy(O).to(t["q"].dtype))
+    lse = to_dev(torch.from_numpy(L).float())
+    q, k, v, do = (to_dev(t[n]) for n in ("q", "k", "v", "do"))
+    g = eta.attn_bwd(q, k, v, o, lse, do, scale=prm["scale"], causal=prm["causal"], dropout_p=p, seed=seed,
+                     offset=offset, deterministic=deterministic, dq_splits=dq_splits)
+    torch.cuda.synchronize()
+    return tuple(x.cpu() for x in g)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,p", [
+    (1, 4, 2, 257, 193, 0.15),
+    (1, 2, 2, 300, 100, 0.4),      # causal rows with no visible key
+])
+def test_dropout_backward_elementwise(deterministic, dtype, d, causal, B, Hq, Hkv, Sq, Sk, p):
+    need_gpu()
+    w = attn_inputs.prefill(B, Hq, Hkv, Sq, Sk, d, dtype, seed=900 + Sq + d, causal=causal, with_grad=True)
+    t, prm = w.tensors, w.params
+    seed, offset = 4242 + Sk, 1
+    say(f"[dropout-bwd] {w.name} causal={causal} p={p} det={deterministic}")
+    got = _dropout_grads(w, p, seed, offset, deterministic)
+    ref = dropout.backward(t["q"], t["k"], t["v"], t["do"], prm["scale"], causal, p, seed, offset,
+                           o_storage=t["q"].dtype)
+    errs = [assert_close_out(g_, r_, TOL_GRAD, f"{w.name} {n}") for n, g_, r_ in zip(("dq", "dk", "dv"), got, ref)]
+    say("    max err dq/dk/dv = " + " ".join(f"{e:.2e}" for e in errs))
+
+
+def test_dropout_backward_deterministic_repeatable_and_split():
+    need_gpu()
+    w = attn_inputs.prefill(1, 8, 2, 500, 700, 128, "bf16", seed=91, causal=True, with_grad=True)
+    a = _dropout_grads(w, 0.3, 77, 5, True, 4)
+    b = _dropout_grads(w, 0.3, 77, 5, True, 4)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    t, prm = w.tensors, w.params
+    ref = dropout.backward(t["q"], t["k"], t["v"], t["do"], prm["scale"], True, 0.3, 77, 5, o_storage=t["q"].dtype)
+    for g_, r_ in zip(a, ref):
+        assert_close_out(g_, r_, TOL_GRAD, w.name)
