@@ -80,12 +80,16 @@ def _fwd_flops(B, Hq, Sq, Sk, d, causal):
     return f / 2 if causal else f
 
 
-def bench_fwd(name, w, steps, warmup, torch, eta):
+def bench_fwd(name, w, steps, warmup, torch, eta, dropout_p=None):
     t, p = w.tensors, w.params
     q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    fn = lambda: eta.attn_fwd(q, k, v, scale=p["scale"], causal=p["causal"], o=o, lse=lse)
+    if dropout_p is None:
+        fn = lambda: eta.attn_fwd(q, k, v, scale=p["scale"], causal=p["causal"], o=o, lse=lse)
+    else:
+        fn = lambda: eta.attn_fwd_dropout(q, k, v, dropout_p, 1234, 0, scale=p["scale"], causal=p["causal"],
+                                          o=o, lse=lse)
     per, region = _time_launches(fn, steps, warmup, torch)
     flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
     med = region / steps
@@ -94,7 +98,7 @@ def bench_fwd(name, w, steps, warmup, torch, eta):
             "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}, (q, k, v, o, lse)
 
 
-def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False):
+def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False, dropout_p=None):
     t, p = w.tensors, w.params
     q, k, v, o, lse = fwd_bufs
     do = t["do"].cuda()
@@ -109,7 +113,7 @@ def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False)
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"],
                               grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv,
-                              deterministic=deterministic)
+                              deterministic=deterministic, dropout_p=dropout_p, seed=1234, offset=0)
     per, region = _time_launches(fn, steps, warmup, torch)
     flops = 2.5 * _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
     med = region / steps
@@ -270,6 +274,15 @@ def main():
                                                             deterministic=True)
             except eta.AttnError as e:
                 configs["c3_bwd_deterministic"] = {"error": str(e)}
+            try:
+                r, dbufs = bench_fwd(name + " fwd, dropout 0.1", w3, max(5, args.steps // 3), 2, torch, eta,
+                                     dropout_p=0.1)
+                configs["c3_fwd_dropout"] = r
+                configs["c3_bwd_dropout"] = bench_bwd(name + " bwd, dropout 0.1", w3, dbufs,
+                                                      max(3, args.steps // 5), 1, torch, eta, dropout_p=0.1)
+                del dbufs
+            except eta.AttnError as e:
+                configs["c3_fwd_dropout"] = {"error": str(e)}
             del bufs, w3
             torch.cuda.empty_cache()
             _log("[bench] c3 packed variable-length prefill fwd")
