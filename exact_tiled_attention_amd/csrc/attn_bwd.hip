@@ -292,6 +292,29 @@ void bwd_main_kernel(BwdArgs a) {
   // MASKED applies the element mask (tails and the causal band).
   auto compute = [&](auto masked_tag, int qt, int h) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    // Dropout decisions, first (their temporaries never meet the products' registers),
+    // as bit 4t + i for query 16t + 4g + i.  The lane's key is mykey; the four lanes of a
+    // key quad (n = 4a .. 4a+3) share the Philox counter word mykey / 4, so each computes
+    // the call of query (t, n % 4) only and the words move by shuffles: in round r a lane
+    // sends word (n + r) % 4 of its call and receives, from quad lane (n - r) % 4, word
+    // n % 4 (= mykey % 4) of query (t, (n - r) % 4).
+    uint32_t keepbits = 0;
+    if constexpr (DROP) {
+      const int e = n & 3;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qt * BQ + 16 * t + 4 * g + e),
+                                       (uint32_t)(b * a.Hq + h), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int wi = (e + r) & 3;
+          const uint32_t send = wi == 0 ? wv[0] : wi == 1 ? wv[1] : wi == 2 ? wv[2] : wv[3];
+          const uint32_t got = (uint32_t)__shfl((int)send, (lane & ~3) | ((e - r) & 3));
+          keepbits |= (got >= a.drop.thresh ? 1u : 0u) << (4 * t + ((e - r) & 3));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const uint8_t* sq = lds + L::Q;
     const uint8_t* sdo = lds + L::DO;
     // S, dP: tile t = query rows 16t .. 16t+15; lane holds queries 16t + 4g + i.  The
@@ -331,12 +354,7 @@ void bwd_main_kernel(BwdArgs a) {
         }
         float z = 1.f;
         if constexpr (DROP) {
-          // key mykey of query row qr: word mykey % 4 of counter (mykey / 4, qr, b Hq + h, offset)
-          const int qr = qt * BQ + qb + i;
-          const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)qr, (uint32_t)(b * a.Hq + h),
-                                         a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
-          const uint32_t word = (mykey & 3) == 0 ? wv[0] : (mykey & 3) == 1 ? wv[1] : (mykey & 3) == 2 ? wv[2] : wv[3];
-          z = word >= a.drop.thresh ? a.drop.rp : 0.f;
+          z = ((keepbits >> (4 * t + i)) & 1u) ? a.drop.rp : 0.f;
         }
         s[t][i] = pv * z;
         dp[t][i] = pv * (z * dp[t][i] - dl[i]);
@@ -579,6 +597,19 @@ void bwd_dq_kernel(BwdArgs a) {
     const uint8_t* vs = lds + (2 + slot) * TB;
 #pragma unroll 1
     for (int kbk = 0; kbk < KB; ++kbk) {
+      // dropout decisions of this key block, first: bit i for register i (registers
+      // 4q .. 4q+3 are four consecutive keys, one Philox call each q)
+      uint32_t keepbits = 0;
+      if constexpr (DROP) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u32x4 wv = philox4x32_10((uint32_t)(t * (BC / 4) + 8 * kbk + 2 * q4 + grp), (uint32_t)qrow,
+                                         (uint32_t)(b * a.Hq + h), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) keepbits |= (wv[e] >= a.drop.thresh ? 1u : 0u) << (4 * q4 + e);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       f32x16 sc, dp;
       const int row = kbk * 32 + n;
 #pragma unroll
@@ -590,25 +621,16 @@ void bwd_dq_kernel(BwdArgs a) {
         dp = E::mfma(av, df[kc], kc == 0 ? f32x16{} : dp);
         if ((kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
       }
-      // P and dS; register i is key t BC + 32 kbk + 8(i/4) + 4 grp + i%4, so registers
-      // 4q .. 4q+3 are four consecutive keys: one Philox call decides them (dropout)
+      // P and dS; register i is key t BC + 32 kbk + 8(i/4) + 4 grp + i%4
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x4 wv = {};
-        if constexpr (DROP)
-          wv = philox4x32_10((uint32_t)(t * (BC / 4) + 8 * kbk + 2 * q4 + grp), (uint32_t)qrow,
-                             (uint32_t)(b * a.Hq + h), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q4 + e;
-          float pv = fast_exp2(fmaf(sc[i], a.scale_log2, -lse2));
-          if constexpr (MASK) {
-            const int key = t * BC + 32 * kbk + 8 * (i >> 2) + 4 * grp + (i & 3);
-            pv = key < klim ? pv : 0.f;
-          }
-          const float z = DROP ? (wv[e] >= a.drop.thresh ? a.drop.rp : 0.f) : 1.f;
-          dp[i] = pv * (z * dp[i] - dl);
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(fmaf(sc[i], a.scale_log2, -lse2));
+        if constexpr (MASK) {
+          const int key = t * BC + 32 * kbk + 8 * (i >> 2) + 4 * grp + (i & 3);
+          pv = key < klim ? pv : 0.f;
         }
+        const float z = DROP ? (((keepbits >> i) & 1u) ? a.drop.rp : 0.f) : 1.f;
+        dp[i] = pv * (z * dp[i] - dl);
       }
       // dQ^T += K^T dS^T, key chunk cc: slots of lane group g = keys 16cc + 8(s/4) + 4g + s%4
 #pragma unroll
