@@ -163,3 +163,49 @@ def dequantized(codes, scales, scale_rows: int = 128) -> np.ndarray:
     s = np.asarray(scales.cpu().numpy() if hasattr(scales, "cpu") else scales, dtype=np.float64)
     S = X.shape[2]
     return X * s[:, :, np.arange(S) // scale_rows][..., None]
+
+
+# ---------------------------------------------------------------------------------
+# Incoherent processing and scale granularity ([HW] section 0x06, "Incoherent
+# Processing Is Exact Before Quantization Only" and the block-vs-tensor ablation that
+# follows it).  With R = diag(s) H / sqrt(d) (random signs s, Sylvester Hadamard H) R
+# is orthogonal, so (Q R)(K R)^T = Q K^T in exact arithmetic; V is not transformed.
+# After E4M3 rounding the identity no longer holds and whether the error shrinks
+# depends on the data's geometry.
+
+def hadamard_matrix(d: int) -> np.ndarray:
+    """Normalised Sylvester Hadamard matrix of order d (a power of two): H_1 = [1],
+    H_2n = [[H_n, H_n], [H_n, -H_n]] / sqrt(2) at every doubling."""
+    assert d >= 1 and d & (d - 1) == 0, "order must be a power of two"
+    H = np.ones((1, 1))
+    while H.shape[0] < d:
+        H = np.block([[H, H], [H, -H]]) / math.sqrt(2.0)
+    return H
+
+
+def incoherent(x, signs) -> np.ndarray:
+    """x R along the last axis, R = diag(signs) H / sqrt(d) (orthogonal for +-1 signs)."""
+    X = np.asarray(x.detach().cpu().double().numpy() if hasattr(x, "detach") else x, dtype=np.float64)
+    s = np.asarray(signs, dtype=np.float64)
+    return (X * s) @ hadamard_matrix(X.shape[-1])
+
+
+def quantize(x, block_rows: int = 128, per_tensor: bool = False):
+    """E4M3 codes and float32 descales [B,H,ceil(S/block_rows)] of float64 x [B,H,S,d].
+
+    Block mode: descale = amax(block) / 448 per (b, h, 128-row block) (1 for an all-zero
+    block).  Tensor mode: one descale from the amax of the whole tensor, repeated in
+    every entry.  Codes = E4M3(x / descale) with the descale as stored (float32).
+    """
+    X = np.asarray(x, dtype=np.float64)
+    B, H, S, d = X.shape
+    nb = (S + block_rows - 1) // block_rows
+    pad = np.zeros((B, H, nb * block_rows - S, d))
+    Xb = np.concatenate([X, pad], axis=2).reshape(B, H, nb, block_rows, d)
+    if per_tensor:
+        amax = np.full((B, H, nb), np.abs(X).max() if X.size else 0.0)
+    else:
+        amax = np.abs(Xb).max(axis=(3, 4))
+    desc = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32).astype(np.float64)
+    codes = encode_rne_sat(Xb / desc[..., None, None]).reshape(B, H, nb * block_rows, d)[:, :, :S]
+    return codes, desc.astype(np.float32)
