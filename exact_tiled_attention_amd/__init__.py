@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -115,6 +115,24 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                total_q, total_k, d, scale, int(bool(causal)), _code(q.dtype), _stream(stream))
     _lib.check("attn_fwd_varlen", st)
     return o, lse
+
+
+def fp8_quantize(x, signs=None, per_tensor=False, codes=None, descale=None, stream=None):
+    """E4M3 codes [B,H,S,d] (uint8) and float32 descales [B,H,ceil(S/128)] of x (fp16/bf16),
+    optionally after the incoherent transform x diag(signs) H / sqrt(d) (signs: float32 [d])."""
+    _require(x, "x", 4)
+    B, H, S, d = x.shape
+    nb = (S + 127) // 128
+    codes = torch.empty((B, H, S, d), dtype=torch.uint8, device=x.device) if codes is None else codes
+    descale = torch.empty((B, H, nb), dtype=torch.float32, device=x.device) if descale is None else descale
+    _expect(codes, "codes", (B, H, S, d), torch.uint8, x.device)
+    _expect(descale, "descale", (B, H, nb), torch.float32, x.device)
+    if signs is not None:
+        _expect(signs, "signs", (d,), torch.float32, x.device)
+    st = lib().attn_fp8_quantize(_ptr(x), _code(x.dtype), B, H, S, d, _ptr(signs), int(bool(per_tensor)),
+                                 _ptr(codes), _ptr(descale), _stream(stream))
+    _lib.check("attn_fp8_quantize", st)
+    return codes, descale
 
 
 def fp8_kv_tile() -> int:

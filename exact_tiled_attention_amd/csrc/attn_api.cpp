@@ -151,6 +151,22 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 
 int attn_fp8_kv_tile(void) { return attn_fp8_tile_keys(); }
 
+int attn_fp8_quantize(const void* x, attn_dtype_t dtype, int B, int H, int S, int d,
+                      const float* signs, int per_tensor, unsigned char* codes, float* descale,
+                      void* stream) {
+  if (x == nullptr || codes == nullptr || descale == nullptr) return ATTN_ERR_NULL;
+  if (B <= 0 || H <= 0 || S <= 0 || S > kMaxSeq || (int64_t)B * H > 65535) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  QuantArgs a = {};
+  a.x = x; a.signs = signs; a.codes = codes; a.descale = descale;
+  a.B = B; a.H = H; a.S = S; a.d = d;
+  a.nblk = (S + 127) / 128;
+  a.per_tensor = per_tensor != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  return hip_status(attn_launch_fp8_quantize(a, (hipStream_t)stream));
+}
+
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  const float* q_scale, const float* k_scale, const float* v_scale,
                  void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,

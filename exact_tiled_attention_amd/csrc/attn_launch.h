@@ -94,7 +94,18 @@ struct DecodeArgs {
   int max_pages, num_pages, page_shift;
 };
 
+struct QuantArgs {
+  const void* x;          // [B, H, S, d] element type
+  const float* signs;     // [d] +-1, or null: no transform
+  uint8_t* codes;         // [B, H, S, d] E4M3
+  float* descale;         // [B, H, nblk] float32
+  int B, H, S, d, nblk;
+  int per_tensor;
+  int dtype_bf16;
+};
+
 hipError_t attn_launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t attn_launch_fp8_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int attn_fp8_tile_keys();
 hipError_t attn_launch_bwd(const BwdArgs& a, hipStream_t stream);

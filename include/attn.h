@@ -126,6 +126,27 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fp8_quantize -- E4M3 codes and descales for attn_fwd_fp8, with optional
+ * incoherent processing.  "M4.6 - FlashAttention-3/4 Hardware Pipelines ...", section
+ * 0x06: scales per 128-row block of one (batch, head), or one per tensor (the
+ * granularity ablation); for Q and K the optional right transform R = diag(signs) H /
+ * sqrt(d) with the Sylvester Hadamard H (orthogonal: (Q R)(K R)^T = Q K^T before
+ * quantisation; give Q and K the same signs and do not transform V).
+ *
+ *   x [B, H, S, d] element type `dtype` (ATTN_F16 / ATTN_BF16), d = 64 or 128   (in)
+ *   signs: device float32 [d] of +-1, or NULL for no transform                   (in)
+ *   per_tensor: 0: descale = amax(block) / 448 per (b, h, 128-row block) (1 for an
+ *       all-zero block); 1: one descale from the amax of the whole tensor, written to
+ *       every entry
+ *   codes [B, H, S, d] E4M3FN bytes = round-to-nearest-even of (x R) / descale,
+ *       clamped to +-448                                                          (out)
+ *   descale [B, H, ceil(S / 128)] float32                                         (out)
+ */
+int attn_fp8_quantize(const void* x, attn_dtype_t dtype, int B, int H, int S, int d,
+                      const float* signs, int per_tensor, unsigned char* codes, float* descale,
+                      void* stream);
+
+/*
  * attn_fwd_fp8 -- forward on E4M3FN operands with per-block descales.
  * "M4.6 - FlashAttention-3/4 Hardware Pipelines", section 0x06 ("Derive Where Every
  * Scale Must Enter"; "Why The Source Raises Softmax Probabilities By 2^8"):

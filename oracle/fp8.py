@@ -195,7 +195,9 @@ def quantize(x, block_rows: int = 128, per_tensor: bool = False):
 
     Block mode: descale = amax(block) / 448 per (b, h, 128-row block) (1 for an all-zero
     block).  Tensor mode: one descale from the amax of the whole tensor, repeated in
-    every entry.  Codes = E4M3(x / descale) with the descale as stored (float32).
+    every entry.  Codes = E4M3(x / descale) with the descale as stored (float32); the
+    quotient that decides the code is formed in float32, the precision of the kernel
+    (the pages fix none for it), and then rounded to nearest even.
     """
     X = np.asarray(x, dtype=np.float64)
     B, H, S, d = X.shape
@@ -206,6 +208,7 @@ def quantize(x, block_rows: int = 128, per_tensor: bool = False):
         amax = np.full((B, H, nb), np.abs(X).max() if X.size else 0.0)
     else:
         amax = np.abs(Xb).max(axis=(3, 4))
-    desc = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32).astype(np.float64)
-    codes = encode_rne_sat(Xb / desc[..., None, None]).reshape(B, H, nb * block_rows, d)[:, :, :S]
-    return codes, desc.astype(np.float32)
+    desc = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+    u = Xb.astype(np.float32) / desc[..., None, None]          # float32, correctly rounded
+    codes = encode_rne_sat(u.astype(np.float64)).reshape(B, H, nb * block_rows, d)[:, :, :S]
+    return codes, desc
