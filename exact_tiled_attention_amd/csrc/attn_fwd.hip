@@ -132,11 +132,24 @@ void fwd_kernel(FwdArgs a) {
 
   const int BH = a.B * a.Hq;
   const int wg = blockIdx.x;
+  // Workgroups go round-robin to the 8 XCDs (each with its own L2).  Padded layout:
+  // the K/V head index (b, kvh) varies fastest, so the g query heads sharing a K/V head
+  // land on the same XCD whenever B Hkv is a multiple of 8.  Packed layout: the heads
+  // of one sequence stay adjacent (sequences differ in length; measured faster).
   const int bh = wg % BH;
   const int qt = CAUSAL ? (a.nqt - 1 - wg / BH) : (wg / BH);   // heavy causal tiles first
-  const int b = bh / a.Hq;
-  const int h = bh - b * a.Hq;
-  const int kvh = h / a.group;
+  int b, h, kvh;
+  if constexpr (VL) {
+    b = bh / a.Hq;
+    h = bh - b * a.Hq;
+    kvh = h / a.group;
+  } else {
+    const int nkv = a.B * a.Hkv;
+    const int bkv = bh % nkv;
+    b = bkv / a.Hkv;
+    kvh = bkv - b * a.Hkv;
+    h = kvh * a.group + bh / nkv;
+  }
 
   // Geometry of this (sequence, head): lengths, first-row element offsets, row strides
   // (d for the padded layout, H d for the packed token-major layout), LSE row base.
