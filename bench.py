@@ -38,8 +38,10 @@ def measured_traffic():
     import hashlib
     try:
         kv = dict(line.split(" = ", 1) for line in open(TRAFFIC_FILE).read().splitlines() if " = " in line)
-        src = open(os.path.join(ROOT, kv["kernel_source"].strip()), "rb").read()
-        if hashlib.sha256(src).hexdigest()[:16] != kv["kernel_source_sha256_16"].strip():
+        h = hashlib.sha256()
+        for name in kv["kernel_source"].split(","):        # the kernel file and its headers
+            h.update(open(os.path.join(ROOT, name.strip()), "rb").read())
+        if h.hexdigest()[:16] != kv["kernel_source_sha256_16"].strip():
             return None
         return int(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -221,8 +223,8 @@ def cpu_baseline(w, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only", default=None, help="run only this extra workload (c3, c4, c5)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")

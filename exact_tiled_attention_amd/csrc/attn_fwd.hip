@@ -20,13 +20,14 @@
 // slot j of lane group g in key chunk c is key 16c + 8(j/4) + 4g + j%4, the same
 // keys the S^T accumulator put in registers 8(c%2) .. 8(c%2)+7.
 //
-// Staging.  K and V tiles are staged row-major in LDS through registers, K and V in
-// rings of two slots each.  The V^T operand of the P V product comes from
+// Staging.  K and V tiles are loaded row-major from HBM straight into LDS (buffer loads
+// with the LDS destination, no staging registers), K and V in rings of two slots
+// each.  The V^T operand of the P V product comes from
 // ds_read_b64_tr_b16, which hands each lane of a 16-lane group one column of a 4-row
 // x 16-column block (4 consecutive keys of one d), so V needs no transpose on the way
 // in.  Rows are not padded; each row's 16-byte chunks are XOR-swizzled instead (LDS
 // chunk p of row r holds global chunk p ^ swz(r)), with swizzles chosen so that the
-// K reads, the V transpose reads and the 16-byte tile writes all hit distinct banks.
+// K fragment reads and the V transpose reads hit distinct banks.
 //
 // Software pipeline.  Step t of a wave runs, chunk by chunk over the 16-key chunks
 // of the tile, the score product of tile t+1, the probabilities of tile t and the
@@ -35,9 +36,9 @@
 // rescale decision) ends the step, under the tail of the P V product.  The rescale of
 // the output accumulator, when one is needed, follows the P V product of tile t,
 // whose terms still belong to the old maximum.  Staging runs one tile ahead: step t
-// writes K(t+2) and V(t+1) into LDS from registers, then loads K(t+3) and V(t+2) into
-// those registers; one workgroup barrier per step publishes the writes of the step
-// before and frees the slots read in it.
+// waits for its own loads of K(t+1) and V(t) (issued a step earlier), passes one
+// workgroup barrier, which publishes every thread's part and frees the slots read in
+// step t-1, then issues the loads of K(t+2) and V(t+1) into those slots.
 //
 // Exponentials run in base 2: p = exp2(s * c - m) with c = scale * log2(e) in one FMA.
 // Masking (key tail and causal band) sets the invisible scores to -inf before the row
@@ -108,7 +109,10 @@ void fwd_kernel(FwdArgs a) {
   constexpr int PC = BC / 16;                 // key chunks of 16 for P V
   constexpr int KPC = KC / PC;                // score contraction chunks per key chunk
   // K/V ring depth: three slots each where the key ranges' rings fit the LDS, else two.
-  constexpr int DEPTH = KS * 6 * TL::BYTES <= 160 * 1024 ? 3 : 2;
+  // K/V ring depth (slots per ring).  Two: with the loop unrolled by two steps the
+  // slots are compile-time constants, so every LDS read address is a fixed register
+  // plus an immediate; three slots (loads two tiles ahead) measured slower.
+  constexpr int DEPTH = 2;
   constexpr int RING = 2 * DEPTH * TL::BYTES; // K slots then V slots
   constexpr int NTK = RW * kWave;             // threads staging one key range
   constexpr int LOADS = TL::CHUNKS / NTK;     // 16-byte K (and V) chunks per thread
@@ -412,25 +416,23 @@ void fwd_kernel(FwdArgs a) {
   const int we = max(tb, min(te, wplan.n_visit));
   const int nr = te - tb;
 
-  // Relative tile i (absolute tb + i) lives in slot i % DEPTH of its ring.  Step i
-  // reads K(i+1) and V(i) and loads K(i+DEPTH) and V(i+DEPTH-1), into the slots that
-  // K(i) and V(i-1) held until step i-1.
+  // Relative tile i (absolute tb + i) lives in slot i % 2 of its ring.  Step i reads
+  // K(i+1) and V(i) and loads K(i+2) and V(i+1), into the slots that K(i) and V(i-1)
+  // held until step i-1.
+  static_assert(DEPTH == 2, "the step schedule below is written for two slots");
   auto load_k = [&](int i) { load_tile(kring, i % DEPTH, kb, tb + i, false); };
   auto load_v = [&](int i) { load_tile(vring, i % DEPTH, vb, tb + i, true); };
-  // Prologue: K0 V0 K1 (then V1 K2 with three slots); K0 is needed first.
+  // Prologue: K0 V0 K1; K0 is needed first, V0 and K1 may stay in flight.
   if (nr > 0) {
     load_k(0);
     load_v(0);
   }
-  if (nr > 1) load_k(1);
-  if constexpr (DEPTH == 3) {
-    if (nr > 1) load_v(1);
-    if (nr > 2) load_k(2);
-  }
-  if (nr >= DEPTH)
-    wait_vmcnt<(2 * DEPTH - 2) * LOADS>();   // the loads issued after K0 may stay in flight
-  else
+  if (nr > 1) {
+    load_k(1);
+    wait_vmcnt<2 * LOADS>();
+  } else {
     wait_vmcnt<0>();
+  }
   __syncthreads();
   f32x16 sa[QB][KB], sb[QB][KB];
   if (tb < we) {
@@ -443,16 +445,12 @@ void fwd_kernel(FwdArgs a) {
   // into `nxt`.
   auto step = [&](auto mask_tag, int i, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
     const int t = tb + i;
-    // K(i+1) and V(i) must have landed: only the previous step's loads (if it issued
-    // a full set) may still be in flight.  The barrier then publishes every thread's
-    // part and frees the slots loaded below.
-    if (DEPTH == 3 && t + 2 < te)
-      wait_vmcnt<2 * LOADS>();
-    else
-      wait_vmcnt<0>();
+    // K(i+1) and V(i), the previous step's loads, must have landed; the barrier then
+    // publishes every thread's part and frees the slots loaded below.
+    wait_vmcnt<0>();
     __syncthreads();
-    if (t + DEPTH < te) load_k(i + DEPTH);
-    if (t + DEPTH - 1 < te) load_v(i + DEPTH - 1);
+    if (t + 2 < te) load_k(i + 2);
+    if (t + 1 < te) load_v(i + 1);
 
     const bool has_cur = t < we;
     const bool has_nxt = t + 1 < we;
