@@ -130,38 +130,40 @@ def bench_decode(name, w, steps, warmup, torch, eta):
     t, p = w.tensors, w.params
     q, kc, vc = (t[n].cuda() for n in ("q", "k", "v"))
     lens = t["seqlens"].cuda()
-    ws = torch.empty(eta.decode_workspace_size(p["B"], p["Hq"], p["Smax"], p["d"], p["chunk"]),
+    chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["Smax"])
+    ws = torch.empty(eta.decode_workspace_size(p["B"], p["Hq"], p["Smax"], p["d"], chunk),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((p["B"], p["Hq"], 1), dtype=torch.float32, device="cuda")
-    fn = lambda: eta.attn_decode_splitkv(q, kc, vc, lens, scale=p["scale"], chunk=p["chunk"], workspace=ws,
+    fn = lambda: eta.attn_decode_splitkv(q, kc, vc, lens, scale=p["scale"], chunk=chunk, workspace=ws,
                                          o=o, lse=lse)
     per, region = _time_launches(fn, steps, warmup, torch)
     total_keys = int(t["seqlens"].sum())
     kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
     med = region / steps
-    return {"workload": name, "kernel": "decode split + merge", "ms_median": med,
+    return {"workload": name + f", chunk {chunk}", "kernel": "decode split + merge", "ms_median": med,
             "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
-            "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
+            "chunk": chunk, "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
 
 
 def bench_decode_paged(name, w, steps, warmup, torch, eta):
     t, p = w.tensors, w.params
     q, kp, vp = (t[n].cuda() for n in ("q", "k_pages", "v_pages"))
     bt, lens = t["block_table"].cuda(), t["seqlens"].cuda()
+    chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["max_pages"] * p["page_size"])
     ws = torch.empty(eta.decode_workspace_size(p["B"], p["Hq"], p["max_pages"] * p["page_size"], p["d"],
-                                               p["chunk"]), dtype=torch.uint8, device="cuda")
+                                               chunk), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((p["B"], p["Hq"], 1), dtype=torch.float32, device="cuda")
-    fn = lambda: eta.attn_decode_paged(q, kp, vp, bt, lens, scale=p["scale"], chunk=p["chunk"], workspace=ws,
+    fn = lambda: eta.attn_decode_paged(q, kp, vp, bt, lens, scale=p["scale"], chunk=chunk, workspace=ws,
                                        o=o, lse=lse)
     per, region = _time_launches(fn, steps, warmup, torch)
     total_keys = int(t["seqlens"].sum())
     kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
     med = region / steps
-    return {"workload": name, "kernel": "paged decode split + merge", "ms_median": med,
+    return {"workload": name + f", chunk {chunk}", "kernel": "paged decode split + merge", "ms_median": med,
             "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
-            "page_size": p["page_size"], "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
+            "chunk": chunk, "page_size": p["page_size"], "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
 
 
 def bench_fwd_varlen(name, w, steps, warmup, torch, eta):
@@ -302,7 +304,7 @@ def main():
             _log("[bench] c4 split-KV decode")
             w4 = attn_inputs.CONFIGS["c4_bf16_decode"]()
             try:
-                configs["c4_decode"] = bench_decode("bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768] chunk 256",
+                configs["c4_decode"] = bench_decode("bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768]",
                                                     w4, args.steps, args.warmup, torch, eta)
             except eta.AttnError as e:
                 configs["c4_decode"] = {"error": str(e)}
@@ -312,7 +314,7 @@ def main():
             w4p = attn_inputs.paged_decode(64, 32, 8, 128, "bf16", seed=4, page_size=128)
             try:
                 configs["c4_decode_paged"] = bench_decode_paged(
-                    "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768] chunk 256, paged pool P=128, "
+                    "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768], paged pool P=128, "
                     "permuted block table", w4p, args.steps, args.warmup, torch, eta)
             except eta.AttnError as e:
                 configs["c4_decode_paged"] = {"error": str(e)}

@@ -209,15 +209,25 @@ def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.flo
     return dq, dk, dv
 
 
-def decode_workspace_size(B, Hq, Smax, d, chunk=256) -> int:
+def decode_pick_chunk(B, Hq, Smax) -> int:
+    """The library's default split size for this shape (attn_decode_pick_chunk)."""
+    return lib().attn_decode_pick_chunk(B, Hq, Smax)
+
+
+def decode_workspace_size(B, Hq, Smax, d, chunk=None) -> int:
+    if chunk is None:
+        chunk = decode_pick_chunk(B, Hq, Smax)
     return lib().attn_decode_workspace_size(B, Hq, Smax, d, chunk)
 
 
-def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=256, workspace=None,
+def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=None, workspace=None,
                         o=None, lse=None, stream=None):
-    """Split-KV decode: q [B,Hq,1,d], caches [B,Hkv,Smax,d], seqlens int32 [B] on device."""
+    """Split-KV decode: q [B,Hq,1,d], caches [B,Hkv,Smax,d], seqlens int32 [B] on device.
+    chunk=None takes the library's choice (decode_pick_chunk)."""
     B, Hq, _, d = q.shape
     Hkv, Smax = k_cache.shape[1], k_cache.shape[2]
+    if chunk is None:
+        chunk = decode_pick_chunk(B, Hq, Smax)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -231,10 +241,11 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=256, wor
     return o, lse
 
 
-def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, chunk=256, workspace=None,
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, chunk=None, workspace=None,
                       o=None, lse=None, stream=None):
     """Split-KV decode over a paged pool: q [B,Hq,1,d], pools [num_pages,Hkv,P,d],
-    block_table int32 [B, max_pages], seqlens int32 [B], all on the device."""
+    block_table int32 [B, max_pages], seqlens int32 [B], all on the device.
+    chunk=None takes the library's choice (decode_pick_chunk over max_pages * P keys)."""
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
         _require(t, n, 4)
     _require(block_table, "block_table", 2)
@@ -251,6 +262,8 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None, chu
     lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
     _expect(o, "o", q.shape, q.dtype, q.device)
     _expect(lse, "lse", (B, Hq, 1), torch.float32, q.device)
+    if chunk is None:
+        chunk = decode_pick_chunk(B, Hq, max_pages * P)
     need = decode_workspace_size(B, Hq, max_pages * P, d, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -254,10 +254,16 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
  *   seqlens_k: device int32[B], 0 <= seqlens_k[b] <= Smax; sequence b attends to
  *       keys [0, seqlens_k[b]) (a length of 0 gives O = 0, LSE = -inf)          (in)
  *   o [B,Hq,1,d] element type `dtype`; lse [B,Hq,1] float32 (may be NULL)      (out)
- *   chunk: keys per split, a positive multiple of 64 (256 is the usual value).
+ *   chunk: keys per split, a positive multiple of 64, at most 4096;
+ *       attn_decode_pick_chunk gives the library's choice for a shape.
  *   workspace: >= attn_decode_workspace_size(B, Hq, Smax, d, chunk) bytes     (scratch)
  */
 size_t attn_decode_workspace_size(int B, int Hq, int Smax, int d, int chunk);
+/* attn_decode_pick_chunk -- the split size this library uses by default for B
+ * sequences of up to Smax keys and Hq query heads: the largest of 1536, 768 keys that
+ * still gives at least 16384 (query head, chunk) pairs at full length, else 256.  Pure
+ * host arithmetic; never fails (256 for non-positive arguments). */
+int attn_decode_pick_chunk(int B, int Hq, int Smax);
 int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         const int* seqlens_k, void* o, float* lse,
                         int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,

@@ -112,6 +112,20 @@ def test_decode_and_fp8_checks():
     assert f8(d=64) == -4 and f8(causal=1) == -8 and f8(odt=0) == -5 and f8(Sk=0) == -2
 
 
+def test_decode_pick_chunk():
+    # pure host arithmetic: the largest of 1536, 768 keys that keeps >= 16384 (query
+    # head, chunk) pairs at full length, else 256
+    lib, _ = _lib()
+    assert lib.attn_decode_pick_chunk(64, 32, 32768) == 1536     # 2048 rows x 22 chunks
+    assert lib.attn_decode_pick_chunk(8, 32, 32768) == 256       # 256 x 43 < 16384 at 768
+    assert lib.attn_decode_pick_chunk(16, 32, 32768) == 768      # 512 x 22 < 16384 <= 512 x 43
+    assert lib.attn_decode_pick_chunk(1, 1, 100) == 256
+    assert lib.attn_decode_pick_chunk(0, 32, 32768) == 256 and lib.attn_decode_pick_chunk(4, 8, -1) == 256
+    for args in ((64, 32, 32768), (16, 32, 32768), (3, 5, 7000)):
+        c = lib.attn_decode_pick_chunk(*args)
+        assert c % 64 == 0 and lib.attn_decode_workspace_size(args[0], args[1], args[2], 128, c) > 0
+
+
 def test_decode_paged_argument_checks():
     lib, _ = _lib()
     ws = lib.attn_decode_workspace_size(2, 8, 4 * 128, 128, 256)

@@ -39,11 +39,14 @@ def test_decode_small_elementwise(dtype, d, Hq, Hkv, chunk):
     _run(w, chunk)
 
 
-def test_decode_long_chunk_and_uneven_lengths():
+@pytest.mark.parametrize("chunk", [512, 768, 1536])
+def test_decode_long_chunk_and_uneven_lengths(chunk):
+    # several 64-key passes per wave; a cache length (5120) that is not a multiple of
+    # the chunk leaves a short last chunk
     need_gpu()
     lens = [5000, 1, 1300, 4097]
-    w = attn_inputs.decode(len(lens), 8, 2, 128, "bf16", seed=77, chunk=512, lengths=lens)
-    _run(w, 512)
+    w = attn_inputs.decode(len(lens), 8, 2, 128, "bf16", seed=77, chunk=256, lengths=lens)
+    _run(w, chunk)
 
 
 def test_decode_config4_full_size_sampled():
@@ -51,7 +54,11 @@ def test_decode_config4_full_size_sampled():
     w = attn_inputs.CONFIGS["c4_bf16_decode"]()
     lens = w.tensors["seqlens"].numpy()
     pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 42, 63})
-    _run(w, 256, batches=pick)
+    import exact_tiled_attention_amd as eta
+    p = w.params
+    chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["Smax"])   # the benchmarked launch
+    assert chunk == 1536
+    _run(w, chunk, batches=pick)
 
 
 def test_decode_bitwise_repeatable():
