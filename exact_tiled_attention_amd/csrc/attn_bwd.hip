@@ -583,8 +583,8 @@ void bwd_dq_kernel(BwdArgs a) {
       const uint32_t left = kv_bytes > off ? (uint32_t)(kv_bytes - off) : 0u;
       const uint32_t kd = __builtin_amdgcn_readfirstlane(lds_offset(lds + slot * TB + (r * NT + w * kWave) * 16));
       const uint32_t vd = __builtin_amdgcn_readfirstlane(lds_offset(lds + (2 + slot) * TB + (r * NT + w * kWave) * 16));
-      lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(kb) + off, left), vo, kd);
-      lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(vb) + off, left), vo, vd);
+      lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(kb) + off, left), vo, 0u, kd);
+      lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(vb) + off, left), vo, 0u, vd);
     }
   };
 

@@ -101,17 +101,18 @@ __device__ inline uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct buffer -> LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
-// address dst + 16 l (dst wave-uniform); out-of-range lanes write zeros.  Issued as an
-// asm statement so that the compiler does not add its own (full) vmcnt waits before
-// LDS reads of the ring: the kernels wait explicitly with wait_vmcnt.  The statement
-// sets M0, which the kernels' compiled code does not otherwise use.
-__device__ inline void lds_load_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t dst) {
+// Direct buffer -> LDS load of 16 bytes per lane from byte voff + soff of the buffer:
+// lane l's bytes land at LDS byte address dst + 16 l (soff and dst wave-uniform);
+// out-of-range lanes write zeros.  Issued as an asm statement so that the compiler does
+// not add its own (full) vmcnt waits before LDS reads of the ring: the kernels wait
+// explicitly with wait_vmcnt.  The statement sets M0, which the kernels' compiled code
+// does not otherwise use.
+__device__ inline void lds_load_16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t dst) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(r), "s"(dst)
+               : "v"(voff), "s"(r), "s"(soff), "s"(dst)
                : "memory", "m0");
 #pragma clang diagnostic pop
 }

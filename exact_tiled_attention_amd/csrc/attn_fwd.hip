@@ -236,7 +236,7 @@ void fwd_kernel(FwdArgs a) {
   // its own loads (vmcnt) and the step's barrier publishes them.  Load round r covers
   // rows r*RS .. r*RS+RS-1 and the swizzles repeat every 16 rows, so a thread's column
   // offset is the same in every round.  Padded layout: one resource over the head's
-  // rows, compile-time row offsets.  Packed layout (runtime row stride): a per-round
+  // rows, the tile's first row in the scalar offset.  Packed layout (runtime row stride): a per-round
   // resource (uniform base and remaining range) with one shared vector offset.
   constexpr int RS = NTK / TL::CPR;
   static_assert(RS % 16 == 0 && NTK % TL::CPR == 0, "load rounds must cover whole swizzle periods");
@@ -246,20 +246,25 @@ void fwd_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, (uint32_t)kv_bytes);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, (uint32_t)kv_bytes);
   const int wsub = tid / kWave;               // wave within this key range's group
-  auto load_tile = [&](uint8_t* ring, int slot, const T* src, int t, bool is_v) {
+  // LDS byte address of this wave's first 16-byte position in each ring (uniform; set
+  // once, so a load's destination is scalar arithmetic on constants)
+  const uint32_t kdst = __builtin_amdgcn_readfirstlane(lds_offset(kring + wsub * kWave * 16));
+  const uint32_t vdst = __builtin_amdgcn_readfirstlane(lds_offset(vring + wsub * kWave * 16));
+  auto load_tile = [&](int slot, const T* src, int t, bool is_v) {
     const uint32_t co = is_v ? co_v : co_k;
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(
-          lds_offset(ring + slot * TL::BYTES + (r * NTK + wsub * kWave) * 16));
+      const uint32_t dst = (is_v ? vdst : kdst) + slot * TL::BYTES + r * NTK * 16;
       if constexpr (VL) {
         // the resource must be uniform (SGPRs): t is, but not provably so
         const int64_t off = (int64_t)(__builtin_amdgcn_readfirstlane(t) * BC + r * RS) * kv_rs * 2;
         const uint32_t left = kv_bytes > off ? (uint32_t)(kv_bytes - off) : 0u;
         lds_load_16(make_rsrc(reinterpret_cast<const uint8_t*>(src) + off, left),
-                    (uint32_t)(trow * kv_rs * 2) + co, dst);
+                    (uint32_t)(trow * kv_rs * 2) + co, 0u, dst);
       } else {
-        lds_load_16(is_v ? vr : kr, (uint32_t)((t * BC + r * RS + trow) * D * 2) + co, dst);
+        // the tile's row offset goes in the scalar offset, the rest is loop-invariant
+        lds_load_16(is_v ? vr : kr, (uint32_t)((r * RS + trow) * D * 2) + co,
+                    (uint32_t)(__builtin_amdgcn_readfirstlane(t) * BC * D * 2), dst);
       }
     }
   };
@@ -420,8 +425,8 @@ void fwd_kernel(FwdArgs a) {
   // K(i+1) and V(i) and loads K(i+2) and V(i+1), into the slots that K(i) and V(i-1)
   // held until step i-1.
   static_assert(DEPTH == 2, "the step schedule below is written for two slots");
-  auto load_k = [&](int i) { load_tile(kring, i % DEPTH, kb, tb + i, false); };
-  auto load_v = [&](int i) { load_tile(vring, i % DEPTH, vb, tb + i, true); };
+  auto load_k = [&](int i) { load_tile(i % DEPTH, kb, tb + i, false); };
+  auto load_v = [&](int i) { load_tile(i % DEPTH, vb, tb + i, true); };
   // Prologue: K0 V0 K1; K0 is needed first, V0 and K1 may stay in flight.
   if (nr > 0) {
     load_k(0);
