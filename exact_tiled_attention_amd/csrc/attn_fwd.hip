@@ -50,7 +50,8 @@
 // the reference maximum may stay stale while the new maximum exceeds it by at most a
 // threshold; numerator and denominator share that reference, so the result is exact):
 // the running max m moves only when some row of the wave sees a score more than
-// TAU = 8 (base 2) above it.  Otherwise alpha = 1 and the O / l rescale is skipped;
+// TAU = 8 (base 2) above it (tested per lane on its raw scores against (m + TAU) / c,
+// the cross-lane maximum is taken only when m moves).  Otherwise alpha = 1 and the O / l rescale is skipped;
 // probabilities then stay below 2^8, well inside fp16 / bf16 range.  The denominator
 // sums the fp32 probabilities (before their rounding to the element type), which
 // keeps the log-sum-exp at fp32 accuracy.
@@ -206,6 +207,7 @@ void fwd_kernel(FwdArgs a) {
   // row max can be taken on the raw accumulator values.
   const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
+  const float inv_c = 1.f / c;
   V8 qf[QB][KC];
 #pragma unroll
   for (int j = 0; j < QB; ++j)
@@ -220,13 +222,16 @@ void fwd_kernel(FwdArgs a) {
     }
 
   f32x16 o[QB][DB];
-  float m_i[QB], l_i[QB];   // running max (base-2 units); this lane's share of l
+  // running max (base-2 units); this lane's share of l; the rescale threshold
+  // (m + TAU) / c in raw score units
+  float m_i[QB], l_i[QB], thr[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[j][i] = f32x16{};
     m_i[j] = -INFINITY;
     l_i[j] = 0.f;
+    thr[j] = -INFINITY;
   }
 
   // Staging: chunk idx = r * NTK + tid of a tile is LDS (row, pos) = (idx / CPR,
@@ -386,17 +391,20 @@ void fwd_kernel(FwdArgs a) {
           r1 = vmax(vmax(r1, u[8 + i]), u[8 + i + 1]);
         }
       }
-      mx[j] = max_pair32(vmax(vmax(r0, r1), vmax(v[7], v[15])) * c);
-      up = up || (mx[j] > m_i[j] + kTau);
+      // this lane's maximum (raw units) against the row's threshold: some row of the
+      // wave passes it exactly when some lane's maximum does
+      mx[j] = vmax(vmax(r0, r1), vmax(v[7], v[15]));
+      up = up || (mx[j] > thr[j]);
     }
     const bool moved = wave_any(up);
     if (moved) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
-        const float m_new = fmaxf(m_i[j], mx[j]);
+        const float m_new = fmaxf(m_i[j], max_pair32(mx[j]) * c);
         // the decision is per wave: a row with nothing visible yet keeps m = -inf, alpha 1
         alpha[j] = (m_new == -INFINITY) ? 1.f : fast_exp2(m_i[j] - m_new);
         m_i[j] = m_new;
+        thr[j] = (m_new + kTau) * inv_c;
         l_i[j] *= alpha[j];
       }
     }
