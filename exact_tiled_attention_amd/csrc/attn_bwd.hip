@@ -192,8 +192,13 @@ void bwd_main_kernel(BwdArgs a) {
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  const int jt = blockIdx.x;                 // key tile
-  const int bkv = blockIdx.y;
+  // Workgroups are dispatched in linear order; the key tile varies slowest so that the
+  // tiles with the most visible query tiles under causal masking (the first ones) start
+  // first and the short ones fill the end (longest first).
+  const int nbkv = a.B * a.Hkv;
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int jt = lin / nbkv;                 // key tile
+  const int bkv = lin - jt * nbkv;
   const int b = bkv / a.Hkv;
   const int kvh = bkv - b * a.Hkv;
   const int k0 = jt * kBKV;
