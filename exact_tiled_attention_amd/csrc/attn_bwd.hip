@@ -183,8 +183,13 @@ void bwd_main_kernel(BwdArgs a) {
   static_assert(SCH >= 1 && SCH * (kNTM / 2) == BQ * CPR, "staging chunks split evenly");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[BQ];
-  __shared__ __attribute__((aligned(16))) float s_del[BQ];
+  // Staged Q / dO tiles and their rows' LSE and D: one buffer with dQ (whose dS^T
+  // staging needs the second barrier of each step anyway), two without, the second in
+  // the dS^T region that only the dQ product uses.
+  __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float s_del[2][BQ];
+  static_assert(DQ || 2 * BQ * L::ROWB <= L::K - L::DST, "second stage fits the dS^T region");
+  auto stage_base = [](int sb) { return sb ? L::DST : L::Q; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,8 +270,8 @@ void bwd_main_kernel(BwdArgs a) {
       sdel = qr < a.Sq ? a.delta[ri] : 0.f;
     }
   };
-  auto store_stage = [&]() {
-    uint8_t* dst = lds + (stage_do ? L::DO : L::Q);
+  auto store_stage = [&](int sb) {
+    uint8_t* dst = lds + stage_base(sb) + (stage_do ? L::DO - L::Q : 0);
 #pragma unroll
     for (int r = 0; r < SCH; ++r) {
       const int idx = r * (kNTM / 2) + st_t;
@@ -274,8 +279,8 @@ void bwd_main_kernel(BwdArgs a) {
       st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), sreg[r]);
     }
     if (tid < BQ) {
-      s_lse[tid] = slse;
-      s_del[tid] = sdel;
+      s_lse[sb][tid] = slse;
+      s_del[sb][tid] = sdel;
     }
   };
   // Transpose read of a staged row-major tile: the 16-lane group reads rows rb .. rb+3
@@ -295,7 +300,7 @@ void bwd_main_kernel(BwdArgs a) {
 
   // One step: S / dP for the wave's keys, P and dS, the dV / dK products, dS^T to LDS.
   // MASKED applies the element mask (tails and the causal band).
-  auto compute = [&](auto masked_tag, int qt, int h) {
+  auto compute = [&](auto masked_tag, int qt, int h, int sb) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     // Dropout decisions, first (their temporaries never meet the products' registers),
     // as bit 4t + i for query 16t + 4g + i.  The lane's key is mykey; the four lanes of a
@@ -320,8 +325,8 @@ void bwd_main_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const uint8_t* sq = lds + L::Q;
-    const uint8_t* sdo = lds + L::DO;
+    const uint8_t* sq = lds + stage_base(sb);
+    const uint8_t* sdo = sq + (L::DO - L::Q);
     // S, dP: tile t = query rows 16t .. 16t+15; lane holds queries 16t + 4g + i.  The
     // K / V fragments of a contraction chunk serve both query tiles.
     f32x4 s[2], dp[2];
@@ -347,8 +352,8 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int qb = 16 * t + 4 * g;
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(&s_lse[qb]);
-      const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[qb]);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(&s_lse[sb][qb]);
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[sb][qb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float pv = fast_exp2(fmaf(s[t][i], a.scale_log2, -lv[i]));
@@ -410,18 +415,23 @@ void bwd_main_kernel(BwdArgs a) {
   for (int step = 0; step < nsteps; ++step) {
     int h, qt;
     step_coords(step, h, qt);
-    // (The first barrier (A) also publishes the K and V tiles.)  The previous step's reads of the staged tiles ended before its barrier (B), and
-    // this step's dS^T writes come after barrier (A): one barrier pair per step.
-    store_stage();
+    // (The first barrier (A) also publishes the K and V tiles.)  With dQ: the previous
+    // step's reads of the staged tiles ended before its barrier (B), and this step's
+    // dS^T writes come after barrier (A): one barrier pair per step.  Without dQ the
+    // stage alternates between two buffers: the one written here was last read in
+    // step - 2, which every wave finished before passing barrier (A) of step - 1, so
+    // one barrier per step suffices.
+    const int sb = DQ ? 0 : (step & 1);
+    store_stage(sb);
     __syncthreads();                                          // (A) stage visible
     if (step + 1 < nsteps) prefetch(step + 1);
 
     const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * BQ > a.Sq;
     if (masked)
-      compute(std::true_type{}, qt, h);
+      compute(std::true_type{}, qt, h, sb);
     else
-      compute(std::false_type{}, qt, h);
-    __syncthreads();                                          // (B) dS^T visible
+      compute(std::false_type{}, qt, h, sb);
+    if constexpr (DQ) __syncthreads();                        // (B) dS^T visible
     if constexpr (DQ)
     // dQ_acc += dS K over the 128 keys: block (query tile tq, d block db) per wave pass;
     // slots = keys 32kc + 4g + i and 32kc + 16 + 4g + i for both operands (A = dS by
