@@ -71,6 +71,16 @@ def test_fp8_config5_full_size_sampled():
     _check(w, rows=rows, heads=[(0, 0), (1, 7), (3, 15)])
 
 
+def test_fp8_eight_wave_tiles_with_tails():
+    # a grid of at least one 256-row workgroup per compute unit takes the eight-wave
+    # launch: here 4 x 32 heads x ceil(600 / 256) = 384 workgroups; query and key tails
+    # (600 = 2 x 256 + 88, 777 keys) and GQA 4
+    need_gpu()
+    w = attn_inputs.fp8_prefill(4, 32, 8, 600, 777, 128, seed=61)
+    rows = np.array([0, 1, 127, 128, 255, 256, 300, 511, 512, 513, 599])
+    _check(w, rows=rows, heads=[(0, 0), (1, 13), (2, 22), (3, 31)])
+
+
 def test_fp8_bitwise_repeatable():
     need_gpu()
     w = attn_inputs.fp8_prefill(1, 4, 4, 512, 512, 128, seed=9)
