@@ -23,4 +23,6 @@ Modules:
   tiles   -- causal tile classes, visit counts, packed-launch census  [pinned]
   dropout -- Philox4x32-10 keep decisions by element coordinates, the dropout
              forward and its backward                              [pinned]
+  exp2soft -- the software exp2 (range reduction, degree-3 relative minimax
+             polynomial fitted by the Remez exchange), float32 emulation [pinned]
 """
