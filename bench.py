@@ -6,7 +6,8 @@ A step is one call of the hot path on the headline workload, fp16 forward
 q,k,v [1,8,4096,64] non-causal (34.36 GFLOP per call).  Inputs are resident in HBM
 before the timed region; the region is bracketed by device synchronisation and
 timed with HIP events recorded on the stream the kernels are launched on.  The
-other workloads (causal GQA prefill forward + backward, split-KV decode, fp8
+other workloads (the headline with 2 or 4 of every 8 softmax exponentials evaluated
+by the software exp2, causal GQA prefill forward + backward, split-KV decode, fp8
 forward) are timed the same way and reported under "configs".
 
 Prints ONE JSON line.
@@ -82,12 +83,15 @@ def _fwd_flops(B, Hq, Sq, Sk, d, causal):
     return f / 2 if causal else f
 
 
-def bench_fwd(name, w, steps, warmup, torch, eta, dropout_p=None):
+def bench_fwd(name, w, steps, warmup, torch, eta, dropout_p=None, exp_emulated=None):
     t, p = w.tensors, w.params
     q, k, v = (t[n].cuda() for n in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    if dropout_p is None:
+    if exp_emulated is not None:
+        fn = lambda: eta.attn_fwd_exp_emulated(q, k, v, exp_emulated, scale=p["scale"], causal=p["causal"],
+                                               o=o, lse=lse)
+    elif dropout_p is None:
         fn = lambda: eta.attn_fwd(q, k, v, scale=p["scale"], causal=p["causal"], o=o, lse=lse)
     else:
         fn = lambda: eta.attn_fwd_dropout(q, k, v, dropout_p, 1234, 0, scale=p["scale"], causal=p["causal"],
@@ -227,7 +231,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--only", default=None, help="run only this extra workload (c3, c4, c5)")
+    ap.add_argument("--only", default=None, help="run only this extra workload (c2, c3, c4, c5)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -261,7 +265,13 @@ def main():
 
     configs = {}
     if not args.no_extra:
-        want = [args.only] if args.only else ["c3", "c4", "c5"]
+        want = [args.only] if args.only else ["c2", "c3", "c4", "c5"]
+        if "c2" in want:
+            for emu in (2, 4):
+                _log(f"[bench] headline with {emu} of 8 exponentials in software")
+                r, _ = bench_fwd(head_name + f", {emu}/8 exponentials by software exp2", w2, args.steps,
+                                 args.warmup, torch, eta, exp_emulated=emu)
+                configs[f"c2_fwd_exp_emulated_{emu}"] = r
         if "c3" in want:
             _log("[bench] c3 causal GQA prefill fwd + bwd")
             w3 = attn_inputs.CONFIGS["c3_bf16_causal_gqa"]()

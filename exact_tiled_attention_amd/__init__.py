@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_exp_emulated", "exp2_soft", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -64,6 +64,40 @@ def attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, stream=None):
                         scale, int(bool(causal)), _code(q.dtype), _stream(stream))
     _lib.check("attn_fwd", st)
     return o, lse
+
+
+def attn_fwd_exp_emulated(q, k, v, emulated_per_8, scale=None, causal=False, o=None, lse=None,
+                          stream=None):
+    """attn_fwd with emulated_per_8 (0, 2 or 4) of every 8 softmax exponentials evaluated by
+    the software exp2 on the FMA pipe instead of the exponential unit."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n, 4)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    _expect(k, "k", (B, Hkv, Sk, d), q.dtype, q.device)
+    _expect(v, "v", (B, Hkv, Sk, d), q.dtype, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, Sq), torch.float32, q.device)
+    st = lib().attn_fwd_exp_emulated(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                     Sq, Sk, d, scale, int(bool(causal)), _code(q.dtype),
+                                     int(emulated_per_8), _stream(stream))
+    _lib.check("attn_fwd_exp_emulated", st)
+    return o, lse
+
+
+def exp2_soft(x, y=None, stream=None):
+    """y = software exp2 of a float32 tensor x (the forward's emulated exponential)."""
+    _require(x, "x", x.dim())
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    y = torch.empty_like(x) if y is None else y
+    _expect(y, "y", x.shape, torch.float32, x.device)
+    st = lib().attn_exp2_soft(_ptr(x), _ptr(y), x.numel(), _stream(stream))
+    _lib.check("attn_exp2_soft", st)
+    return y
 
 
 def attn_fwd_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False, o=None, lse=None,

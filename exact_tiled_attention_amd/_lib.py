@@ -20,10 +20,13 @@ _F = ctypes.c_float
 _S = ctypes.c_size_t
 _U64 = ctypes.c_ulonglong
 _U32 = ctypes.c_uint
+_LL = ctypes.c_longlong
 
 PROTOTYPES = {
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "attn_fwd_exp_emulated": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "attn_exp2_soft": (_I, [_P, _P, _LL, _P]),
     "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_fp8_kv_tile": (_I, []),
     "attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),

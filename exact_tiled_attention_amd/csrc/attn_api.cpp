@@ -79,6 +79,33 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
 }
 
+int attn_fwd_exp_emulated(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                          attn_dtype_t dtype, int emulated_per_8, void* stream) {
+  if (emulated_per_8 != 0 && emulated_per_8 != 2 && emulated_per_8 != 4) return ATTN_ERR_ARG;
+  if (q == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (Sk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, true);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  FwdArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = dtype == ATTN_BF16;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.exp_emulated = emulated_per_8;
+  return hip_status(attn_launch_fwd(a, (hipStream_t)stream));
+}
+
+int attn_exp2_soft(const float* x, float* y, long long n, void* stream) {
+  if (n < 0 || n > (1LL << 31)) return ATTN_ERR_SHAPE;
+  if (n > 0 && (x == nullptr || y == nullptr)) return ATTN_ERR_NULL;
+  return hip_status(attn_launch_exp2_soft(x, y, (int64_t)n, (hipStream_t)stream));
+}
+
 // Dropout parameters from (p, seed, offset); p must be in [0, 1).
 bool make_drop(float p, unsigned long long seed, unsigned offset, DropParams* dp) {
   if (!(p >= 0.f && p < 1.f)) return false;

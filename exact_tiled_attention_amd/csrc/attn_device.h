@@ -75,6 +75,21 @@ __device__ inline float wave_sum_xor32(float x) { return x + __shfl_xor(x, 32); 
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Software exp2 on the FMA pipe ("M4.6 - FlashAttention-3/4 Hardware Pipelines",
+// section 0x09): x = n + f with n = floor(x) and f in [0, 1); 2^f from the degree-3
+// polynomial that minimises the maximum relative error on [0, 1] (coefficients fitted
+// for this library by the Remez exchange, 7.5e-5), scaled by 2^n through the exponent.
+// Arguments below -150 (and -inf) give 0; a NaN argument gives 0 as well.
+__device__ inline float soft_exp2(float x) {
+  x = fmaxf(x, -150.f);
+  const float n = __builtin_floorf(x);
+  const float f = x - n;
+  float p = fmaf(0.07802452147006989f, f, 0.22606715559959412f);
+  p = fmaf(p, f, 0.6958335638046265f);
+  p = fmaf(p, f, 0.9999251961708069f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
 // 16-bit lane interleave helpers for the register transpose of 4 rows x 8 columns.
 // lo16(a) | lo16(b) << 16  and  hi16(a) | hi16(b) << 16.
 __device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }

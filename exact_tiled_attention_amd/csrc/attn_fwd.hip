@@ -95,8 +95,9 @@ __device__ inline float max_pair32(float x) {
 }
 
 // VL: packed variable-length layout.  DROP: dropout on the probabilities entering P V
-// (padded layout only).
-template <typename T, int D, int QB, int RW, int KS, bool VL, bool CAUSAL, bool DROP>
+// (padded layout only).  EMU: 0, 2 or 4 of every 8 exponentials of a key chunk by the
+// software exp2 on the FMA pipe (padded layout without dropout only).
+template <typename T, int D, int QB, int RW, int KS, bool VL, bool CAUSAL, bool DROP, int EMU = 0>
 __global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
@@ -340,7 +341,8 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const float e0 = fast_exp2(fmaf(sc[kbk][hb + 2 * jj], c, -m_use));
-      const float e1 = fast_exp2(fmaf(sc[kbk][hb + 2 * jj + 1], c, -m_use));
+      const float x1 = fmaf(sc[kbk][hb + 2 * jj + 1], c, -m_use);
+      const float e1 = (EMU == 4 || (EMU == 2 && (jj & 1))) ? soft_exp2(x1) : fast_exp2(x1);
       l0 += e0;
       l1 += e1;
       if constexpr (DROP) {
@@ -601,6 +603,10 @@ hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
       hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true, false>), grid, block, 0, stream, a);
     else if (a.dropout)
       hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, true>), grid, block, 0, stream, a);
+    else if (a.exp_emulated == 2)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false, 2>), grid, block, 0, stream, a);
+    else if (a.exp_emulated == 4)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false, 4>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false>), grid, block, 0, stream, a);
   } else {
@@ -608,6 +614,10 @@ hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
       hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false, false>), grid, block, 0, stream, a);
     else if (a.dropout)
       hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, true>), grid, block, 0, stream, a);
+    else if (a.exp_emulated == 2)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false, 2>), grid, block, 0, stream, a);
+    else if (a.exp_emulated == 4)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false, 4>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false>), grid, block, 0, stream, a);
   }
@@ -632,7 +642,19 @@ hipError_t launch_fwd_dtype(const FwdArgs& a, hipStream_t stream) {
   return launch_fwd_t<T, 128, 1, 4, 2>(a, stream);
 }
 
+// soft_exp2 element by element (the forward's software exponential, callable on its own)
+__global__ __launch_bounds__(256) void exp2_soft_kernel(const float* x, float* y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = soft_exp2(x[i]);
+}
+
 }  // namespace
+
+hipError_t attn_launch_exp2_soft(const float* x, float* y, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(exp2_soft_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError();
+}
 
 hipError_t attn_launch_fwd(const FwdArgs& a, hipStream_t stream) {
   if (a.dtype_bf16) return launch_fwd_dtype<bf16>(a, stream);

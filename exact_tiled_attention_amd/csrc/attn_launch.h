@@ -28,6 +28,7 @@ struct FwdArgs {
   int total_q, total_k;
   int dropout;        // 1: apply dropout with `drop` (padded layout only)
   DropParams drop;
+  int exp_emulated;   // 0, 2 or 4 of every 8 exponentials by soft_exp2 (padded, no dropout)
 };
 
 struct Fp8Args {
@@ -105,6 +106,7 @@ struct QuantArgs {
 };
 
 hipError_t attn_launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t attn_launch_exp2_soft(const float* x, float* y, int64_t n, hipStream_t stream);
 hipError_t attn_launch_fp8_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int attn_fp8_tile_keys();

@@ -78,6 +78,30 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fwd_exp_emulated -- attn_fwd with part of the softmax exponentials computed in
+ * software on the FMA pipe instead of the hardware exponential ("M4.6 - FlashAttention-
+ * 3/4 Hardware Pipelines ...", section 0x09: exp-throughput relief).  The software
+ * exp2 reduces x = n + f (n = floor(x), f in [0, 1)), evaluates a degree-3 polynomial
+ * for 2^f whose coefficients minimise the maximum relative error on [0, 1] (7.5e-5;
+ * fitted for this library by the Remez exchange) and scales by 2^n; see attn_exp2_soft.
+ * The result differs from attn_fwd by that error on the emulated probabilities.
+ *
+ *   Arguments as attn_fwd, plus emulated_per_8: 0, 2 or 4 of every 8 exponentials of a
+ *   key chunk are emulated (else ATTN_ERR_ARG); 0 is attn_fwd exactly.
+ */
+int attn_fwd_exp_emulated(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                          attn_dtype_t dtype, int emulated_per_8, void* stream);
+
+/*
+ * attn_exp2_soft -- the software exp2 of attn_fwd_exp_emulated, element by element:
+ * y[i] = soft_exp2(x[i]) in float32 (fused multiply-adds in Horner order; arguments
+ * at or below -150, -inf included, give 0; results below 2^-126 may be flushed to 0).  x, y: device float32 [n], 0 <= n <= 2^31 (else
+ * ATTN_ERR_SHAPE); asynchronous on `stream`.
+ */
+int attn_exp2_soft(const float* x, float* y, long long n, void* stream);
+
+/*
  * attn_fwd_dropout -- attn_fwd with attention dropout on the probabilities.
  * "M4.4 - FlashAttention-2 ...", section 0x03I and "M4.3 - IO-Aware Attention ...",
  * section 0x0DF: the maximum, the denominator and the LSE stay those of the undropped

@@ -58,6 +58,20 @@ def test_fwd_argument_checks():
     assert call(scale=float("inf")) == -8 and call(scale=float("nan")) == -8
 
 
+def test_fwd_exp_emulated_and_exp2_soft_checks():
+    lib, _ = _lib()
+    f = lib.attn_fwd_exp_emulated
+    def call(emu, q=P, B=1, d=64):
+        return f(q, P, P, P, None, B, 4, 2, 8, 8, d, 0.125, 0, 0, emu, None)
+    for emu in (1, 3, 5, 8, -2):
+        assert call(emu) == -8
+    assert call(2, q=None) == -1 and call(4, B=0) == -2 and call(2, d=96) == -4
+    g = lib.attn_exp2_soft
+    assert g(P, P, -1, None) == -2 and g(P, P, (1 << 31) + 1, None) == -2
+    assert g(None, P, 5, None) == -1 and g(P, None, 5, None) == -1
+    assert g(None, None, 0, None) == 0          # nothing to compute, no launch
+
+
 def test_fwd_varlen_argument_checks():
     lib, _ = _lib()
     f = lib.attn_fwd_varlen
