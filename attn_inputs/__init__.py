@@ -171,9 +171,9 @@ def paged_decode(B, Hq, Hkv, d, dtype, seed, page_size, lo=1024, hi=32768, chunk
 
 # The five workloads the library is measured on, with their sizes.
 CONFIGS = {
-    "c1_fp16_fwd_small": lambda: prefill(1, 4, 4, 128, 128, 64, "f16", seed=1),
-    "c2_fp16_fwd": lambda: prefill(1, 8, 8, 4096, 4096, 64, "f16", seed=2),
-    "c3_bf16_causal_gqa": lambda: prefill(2, 32, 8, 8192, 8192, 128, "bf16", seed=3, causal=True, with_grad=True),
-    "c4_bf16_decode": lambda: decode(64, 32, 8, 128, "bf16", seed=4),
-    "c5_fp8_fwd": lambda: fp8_prefill(4, 16, 16, 8192, 8192, 128, seed=5),
+    "fwd_f16_1x4x128_d64": lambda: prefill(1, 4, 4, 128, 128, 64, "f16", seed=1),
+    "fwd_f16_1x8x4096_d64": lambda: prefill(1, 8, 8, 4096, 4096, 64, "f16", seed=2),
+    "causal_gqa_bf16_2x32x8192_kv8_d128": lambda: prefill(2, 32, 8, 8192, 8192, 128, "bf16", seed=3, causal=True, with_grad=True),
+    "decode_bf16_b64_hq32_kv8_d128": lambda: decode(64, 32, 8, 128, "bf16", seed=4),
+    "fwd_fp8_4x16x8192_d128": lambda: fp8_prefill(4, 16, 16, 8192, 8192, 128, seed=5),
 }

@@ -231,7 +231,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--only", default=None, help="run only this extra workload (c2, c3, c4, c5)")
+    ap.add_argument("--only", default=None, help="run only this extra workload (exp_emulated, causal_gqa, decode, fp8)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -259,85 +259,85 @@ def main():
         del src, dst
 
     head_name = "fp16 fwd q,k,v [1,8,4096,64] non-causal"
-    w2 = attn_inputs.CONFIGS["c2_fp16_fwd"]()
+    w2 = attn_inputs.CONFIGS["fwd_f16_1x8x4096_d64"]()
     _log("[bench] headline", head_name)
     head, _ = bench_fwd(head_name, w2, args.steps, args.warmup, torch, eta)
 
     configs = {}
     if not args.no_extra:
-        want = [args.only] if args.only else ["c2", "c3", "c4", "c5"]
-        if "c2" in want:
+        want = [args.only] if args.only else ["exp_emulated", "causal_gqa", "decode", "fp8"]
+        if "exp_emulated" in want:
             for emu in (2, 4):
                 _log(f"[bench] headline with {emu} of 8 exponentials in software")
                 r, _ = bench_fwd(head_name + f", {emu}/8 exponentials by software exp2", w2, args.steps,
                                  args.warmup, torch, eta, exp_emulated=emu)
-                configs[f"c2_fwd_exp_emulated_{emu}"] = r
-        if "c3" in want:
-            _log("[bench] c3 causal GQA prefill fwd + bwd")
-            w3 = attn_inputs.CONFIGS["c3_bf16_causal_gqa"]()
+                configs[f"fwd_exp_emulated_{emu}"] = r
+        if "causal_gqa" in want:
+            _log("[bench] causal GQA prefill fwd + bwd")
+            w3 = attn_inputs.CONFIGS["causal_gqa_bf16_2x32x8192_kv8_d128"]()
             name = "bf16 causal GQA q [2,32,8192,128] k,v [2,8,8192,128]"
             r, bufs = bench_fwd(name + " fwd", w3, max(5, args.steps // 3), 2, torch, eta)
-            configs["c3_fwd"] = r
+            configs["causal_gqa_fwd"] = r
             try:
-                configs["c3_bwd"] = bench_bwd(name + " bwd", w3, bufs, max(3, args.steps // 5), 1, torch, eta)
+                configs["causal_gqa_bwd"] = bench_bwd(name + " bwd", w3, bufs, max(3, args.steps // 5), 1, torch, eta)
             except eta.AttnError as e:
-                configs["c3_bwd"] = {"error": str(e)}
+                configs["causal_gqa_bwd"] = {"error": str(e)}
             try:
-                configs["c3_bwd_deterministic"] = bench_bwd(name + " bwd, deterministic", w3, bufs,
+                configs["causal_gqa_bwd_deterministic"] = bench_bwd(name + " bwd, deterministic", w3, bufs,
                                                             max(3, args.steps // 5), 1, torch, eta,
                                                             deterministic=True)
             except eta.AttnError as e:
-                configs["c3_bwd_deterministic"] = {"error": str(e)}
+                configs["causal_gqa_bwd_deterministic"] = {"error": str(e)}
             try:
                 r, dbufs = bench_fwd(name + " fwd, dropout 0.1", w3, max(5, args.steps // 3), 2, torch, eta,
                                      dropout_p=0.1)
-                configs["c3_fwd_dropout"] = r
-                configs["c3_bwd_dropout"] = bench_bwd(name + " bwd, dropout 0.1", w3, dbufs,
+                configs["causal_gqa_fwd_dropout"] = r
+                configs["causal_gqa_bwd_dropout"] = bench_bwd(name + " bwd, dropout 0.1", w3, dbufs,
                                                       max(3, args.steps // 5), 1, torch, eta, dropout_p=0.1)
                 del dbufs
             except eta.AttnError as e:
-                configs["c3_fwd_dropout"] = {"error": str(e)}
+                configs["causal_gqa_fwd_dropout"] = {"error": str(e)}
             del bufs, w3
             torch.cuda.empty_cache()
-            _log("[bench] c3 packed variable-length prefill fwd")
+            _log("[bench] packed variable-length prefill fwd")
             lens = attn_inputs.decode_lengths(3, 8, 256, 4096).tolist()
             w3v = attn_inputs.varlen_prefill(lens, lens, 32, 8, 128, "bf16", seed=3, causal=True)
             try:
-                configs["c3_fwd_varlen"] = bench_fwd_varlen(
+                configs["causal_gqa_fwd_varlen"] = bench_fwd_varlen(
                     f"bf16 causal GQA packed Hq=32 Hkv=8 d=128, 8 sequences S~U[256,4096] (total {sum(lens)})",
                     w3v, max(5, args.steps // 3), 2, torch, eta)
             except eta.AttnError as e:
-                configs["c3_fwd_varlen"] = {"error": str(e)}
+                configs["causal_gqa_fwd_varlen"] = {"error": str(e)}
             del w3v
             torch.cuda.empty_cache()
-        if "c4" in want:
-            _log("[bench] c4 split-KV decode")
-            w4 = attn_inputs.CONFIGS["c4_bf16_decode"]()
+        if "decode" in want:
+            _log("[bench] split-KV decode")
+            w4 = attn_inputs.CONFIGS["decode_bf16_b64_hq32_kv8_d128"]()
             try:
-                configs["c4_decode"] = bench_decode("bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768]",
+                configs["decode"] = bench_decode("bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768]",
                                                     w4, args.steps, args.warmup, torch, eta)
             except eta.AttnError as e:
-                configs["c4_decode"] = {"error": str(e)}
+                configs["decode"] = {"error": str(e)}
             del w4
             torch.cuda.empty_cache()
-            _log("[bench] c4 paged split-KV decode")
+            _log("[bench] paged split-KV decode")
             w4p = attn_inputs.paged_decode(64, 32, 8, 128, "bf16", seed=4, page_size=128)
             try:
-                configs["c4_decode_paged"] = bench_decode_paged(
+                configs["decode_paged"] = bench_decode_paged(
                     "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768], paged pool P=128, "
                     "permuted block table", w4p, args.steps, args.warmup, torch, eta)
             except eta.AttnError as e:
-                configs["c4_decode_paged"] = {"error": str(e)}
+                configs["decode_paged"] = {"error": str(e)}
             del w4p
             torch.cuda.empty_cache()
-        if "c5" in want:
-            _log("[bench] c5 fp8 forward")
-            w5 = attn_inputs.CONFIGS["c5_fp8_fwd"]()
+        if "fp8" in want:
+            _log("[bench] fp8 forward")
+            w5 = attn_inputs.CONFIGS["fwd_fp8_4x16x8192_d128"]()
             try:
-                configs["c5_fp8"] = bench_fp8("fp8 e4m3 fwd [4,16,8192,128] 128-row block scales, bf16 out",
+                configs["fp8_fwd"] = bench_fp8("fp8 e4m3 fwd [4,16,8192,128] 128-row block scales, bf16 out",
                                               w5, max(5, args.steps // 3), 2, torch, eta)
             except eta.AttnError as e:
-                configs["c5_fp8"] = {"error": str(e)}
+                configs["fp8_fwd"] = {"error": str(e)}
             del w5
             torch.cuda.empty_cache()
 

@@ -104,7 +104,8 @@ template <> constexpr bool kSplit<bf16> = true;
 // identity on the row's low four bits; the hardware's conflict counter reads 0 for the
 // fragment reads and 2-way for the transpose reads, against 2-way fragment reads and
 // conflict-free transpose reads for 2(r mod 8) + bit 3 (a wave reads 24 KB of
-// fragments and 16 KB by transpose reads per step; C3 column owner 10 % fewer cycles).  Rows of 128 bytes (d = 64)
+// fragments and 16 KB by transpose reads per step; the causal GQA [2,32,8192,128] column
+// owner takes 10 % fewer cycles).  Rows of 128 bytes (d = 64)
 // pair up in one 256-byte bank span.
 template <int D> __device__ inline int swz_row(int r) {
   if constexpr (D == 128) return r & 15;

@@ -361,7 +361,7 @@ int attn_fp8_tile_keys() { return BC; }
 
 // Eight waves (256 query rows) per workgroup when that still gives every compute unit a
 // workgroup: each staged K/V tile (E4M3 widening, V transpose) then serves twice the
-// rows (C5 2.93 -> 2.37 ms); four otherwise.
+// rows ([4,16,8192,128]: 2.93 -> 2.37 ms); four otherwise.
 hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
   const int64_t wgs256 = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
   if (wgs256 >= 256) return launch_fp8<8>(a, stream);

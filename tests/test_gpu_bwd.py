@@ -82,7 +82,7 @@ def test_bwd_atomic_dq_repeat_within_tolerance():
     assert (a[0] - b[0]).abs().max().item() <= 1e-5                    # dQ: unordered float adds
 
 
-def test_bwd_config3_full_size_one_kv_head():
+def test_bwd_causal_gqa_full_size_one_kv_head():
     need_gpu()
-    w = attn_inputs.CONFIGS["c3_bf16_causal_gqa"]()
+    w = attn_inputs.CONFIGS["causal_gqa_bf16_2x32x8192_kv8_d128"]()
     _check(w, heads=[(1, 5)])

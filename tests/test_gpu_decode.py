@@ -49,9 +49,9 @@ def test_decode_long_chunk_and_uneven_lengths(chunk):
     _run(w, chunk)
 
 
-def test_decode_config4_full_size_sampled():
+def test_decode_b64_full_size_sampled():
     need_gpu()
-    w = attn_inputs.CONFIGS["c4_bf16_decode"]()
+    w = attn_inputs.CONFIGS["decode_bf16_b64_hq32_kv8_d128"]()
     lens = w.tensors["seqlens"].numpy()
     pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 42, 63})
     import exact_tiled_attention_amd as eta

@@ -94,7 +94,7 @@ def test_fwd_exp_emulated_small_elementwise(emu, dtype, d, causal, B, Hq, Hkv, S
 @pytest.mark.parametrize("emu", [2, 4])
 def test_fwd_exp_emulated_full_size_sampled_rows(emu):
     need_gpu()
-    w = attn_inputs.CONFIGS["c2_fp16_fwd"]()
+    w = attn_inputs.CONFIGS["fwd_f16_1x8x4096_d64"]()
     rows = np.unique(np.concatenate([np.arange(0, 4096, 131), [4095]]))
     _check(w, emu, rows=rows)
 

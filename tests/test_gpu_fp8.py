@@ -64,9 +64,9 @@ def test_fp8_small_elementwise(B, Hq, Hkv, Sq, Sk):
     _check(attn_inputs.fp8_prefill(B, Hq, Hkv, Sq, Sk, 128, seed=500 + Sq + Sk))
 
 
-def test_fp8_config5_full_size_sampled():
+def test_fp8_4x16x8192_full_size_sampled():
     need_gpu()
-    w = attn_inputs.CONFIGS["c5_fp8_fwd"]()
+    w = attn_inputs.CONFIGS["fwd_fp8_4x16x8192_d128"]()
     rows = np.unique(np.concatenate([np.arange(0, 8192, 331), [0, 127, 128, 8191]]))
     _check(w, rows=rows, heads=[(0, 0), (1, 7), (3, 15)])
 

@@ -52,9 +52,9 @@ def test_fwd_small_elementwise(dtype, d, causal, B, Hq, Hkv, Sq, Sk):
     _check(w)
 
 
-def test_fwd_config1_listing_shape():
+def test_fwd_listing_shape_1x4x128():
     need_gpu()
-    _check(attn_inputs.CONFIGS["c1_fp16_fwd_small"]())
+    _check(attn_inputs.CONFIGS["fwd_f16_1x4x128_d64"]())
 
 
 def test_fwd_empty_keys_and_zero_scale():
@@ -69,16 +69,16 @@ def test_fwd_empty_keys_and_zero_scale():
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
 
-def test_fwd_config2_full_size_sampled_rows():
+def test_fwd_1x8x4096_full_size_sampled_rows():
     need_gpu()
-    w = attn_inputs.CONFIGS["c2_fp16_fwd"]()
+    w = attn_inputs.CONFIGS["fwd_f16_1x8x4096_d64"]()
     rows = np.unique(np.concatenate([np.arange(0, 4096, 97), [4095]]))
     _check(w, rows=rows)
 
 
-def test_fwd_config3_full_size_sampled():
+def test_fwd_causal_gqa_full_size_sampled():
     need_gpu()
-    w = attn_inputs.CONFIGS["c3_bf16_causal_gqa"]()
+    w = attn_inputs.CONFIGS["causal_gqa_bf16_2x32x8192_kv8_d128"]()
     rows = np.unique(np.concatenate([np.arange(0, 8192, 211), [0, 1, 127, 128, 8191]]))
     heads = [(0, 0), (0, 5), (1, 31), (1, 12)]
     _check(w, rows=rows, heads=heads)
