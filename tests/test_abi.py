@@ -209,3 +209,11 @@ def test_dropout_argument_checks():
         return lib.attn_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 2, 2, 8, 8, 64, 0.125, 0, p, 1, 0, 1, 2, det,
                                     splits, P, ws_bytes, None)
     assert bwd(p=1.0) == -8 and bwd(ws_bytes=ws - 1) == -6 and bwd(det=1, splits=3) == -8
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    from exact_tiled_attention_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattn.so"))
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.lib()
