@@ -59,15 +59,101 @@ def test_without_probability_rounding_steps_reduce_to_dense(block_c):
     assert np.allclose(L, Ld, atol=1e-11)
 
 
-def test_two_to_the_eight_cancels_exactly():
-    rng = np.random.default_rng(3)
-    s = rng.normal(size=50) * 4
-    v = rng.normal(size=(50, 3))
-    m = s.max()
-    u = 2.0 ** 8 * np.exp(s - m)
-    plain = np.exp(s - m)
-    assert np.allclose((u @ v) / u.sum(), (plain @ v) / plain.sum(), atol=1e-15)
-    assert abs((m + math.log(u.sum()) - 8 * math.log(2)) - (m + math.log(plain.sum()))) < 1e-14
+# ---------------------------------------------------------------------------------
+# Hand-derived pins of the probability rounding ([HW] section 0x06, "Why The Source
+# Raises Softmax Probabilities By 2^8" and "Derive Where Every Scale Must Enter").
+# Each case uses head dimension 1 and hand-picked E4M3 codes, so every score is known
+# exactly; the expected O and LSE are written out below from the stated step order:
+# u = 2^8 e^(S - m) in the running-max frame, p8 = E4M3(u) (values typed in by hand
+# from the codebook: sign, 4 exponent bits with bias 7, 3 fraction bits), l from the
+# unrounded u, o += dV_j (p8 . V_j), O = o / l, LSE = m + ln l - 8 ln 2.
+
+C_ZERO, C_ONE, C_TWO, C_FOUR = 0x00, 0x38, 0x40, 0x48     # +0, 1.0, 2.0, 4.0
+C_MINUS_ONE, C_MINUS_EIGHT = 0xB8, 0xD0                     # -1.0, -8.0
+
+
+def _codes(vals):
+    return np.asarray(vals, dtype=np.uint8).reshape(1, 1, -1, 1)
+
+
+def _descales(vals):
+    return np.asarray(vals, dtype=np.float32).reshape(1, 1, -1)
+
+
+def _run(k_codes, v_codes, v_scale, block_c, scale_rows=128, frame="running", prob_round=fp8.round_e4m3):
+    nk = len(k_codes)
+    nblk = -(-nk // scale_rows)
+    O, L = fp8.forward(_codes([C_ONE]), _codes(k_codes), _codes(v_codes), _descales([1.0]),
+                       _descales([1.0] * nblk), _descales(v_scale), 1.0, block_c=block_c,
+                       scale_rows=scale_rows, frame=frame, prob_round=prob_round)
+    return float(O[0, 0, 0, 0]), float(L[0, 0, 0])
+
+
+def test_pin_offset_keeps_a_small_probability():
+    """Scores (0, -8) in one tile.  u = (256, 256 e^-8 = 0.08588); the E4M3 value next
+    to 0.08588 is 1.375 * 2^-4 = 0.0859375, so the second key survives.  Without the
+    offset, e^-8 = 3.4e-4 is below half the smallest subnormal (2^-10) and rounds to 0."""
+    O, L = _run([C_ZERO, C_MINUS_EIGHT], [C_ONE, C_TWO], [1.0], block_c=2)
+    e8 = math.exp(-8.0)
+    l = 256.0 * (1.0 + e8)
+    want_O = (256.0 * 1.0 + 0.0859375 * 2.0) / l
+    want_L = math.log(l) - 8 * math.log(2.0)          # m = 0
+    assert abs(O - want_O) < 1e-13 and abs(L - want_L) < 1e-13
+    # the planted mistake -- rounding e^(S - m) first, then applying 2^8 -- loses key 1
+    wrong, _ = _run([C_ZERO, C_MINUS_EIGHT], [C_ONE, C_TWO], [1.0], block_c=2,
+                    prob_round=lambda u: 256.0 * fp8.round_e4m3(u / 256.0))
+    assert abs(wrong - 256.0 / l) < 1e-13 and abs(wrong - want_O) > 5e-4
+    # the denominator sums the unrounded u: summing p8 instead moves O and LSE
+    assert abs(want_O - (256.0 + 0.171875) / (256.0 + 0.0859375)) > 1e-7
+
+
+def test_pin_running_frame_when_the_max_moves():
+    """Scores (0, -2 | 2, 1) in two tiles of two keys, V = (1, 2, 4, -1).
+    Tile 1 (m = 0): u = (256, 256 e^-2 = 34.646) -> p8 = (256, 36)   (step 4 in [32, 64)).
+    Tile 2 (m = 2): alpha = e^-2; u = (256, 256 e^-1 = 94.176) -> p8 = (256, 96)
+    (step 8 in [64, 128)).  Rounding in the final frame (m = 2) instead rounds tile 1's
+    (256 e^-2, 256 e^-4) = (34.646, 4.689) to (36, 4.5) (step 0.5 in [4, 8))."""
+    k = [C_ZERO, 0xC0, C_TWO, C_ONE]                        # q = 1: S = (0, -2, 2, 1)
+    v = [C_ONE, C_TWO, C_FOUR, C_MINUS_ONE]
+    O, L = _run(k, v, [1.0], block_c=2)
+    a = math.exp(-2.0)
+    l = a * (256.0 + 256.0 * math.exp(-2.0)) + (256.0 + 256.0 * math.exp(-1.0))
+    o = a * (256.0 * 1.0 + 36.0 * 2.0) + (256.0 * 4.0 + 96.0 * -1.0)
+    assert abs(O - o / l) < 1e-13
+    assert abs(L - (2.0 + math.log(l) - 8 * math.log(2.0))) < 1e-13
+    # the final-frame variant: tile 1 contributes 36 * 1 + 4.5 * 2 in the final scale
+    Of, Lf = _run(k, v, [1.0], block_c=2, frame="final")
+    o_final = (36.0 * 1.0 + 4.5 * 2.0) + (256.0 * 4.0 + 96.0 * -1.0)
+    assert abs(Of - o_final / l) < 1e-13 and abs(Lf - L) < 1e-13
+    assert abs(Of - O) > 1e-3
+    # one tile of four keys (m = 2 from the start) is the final frame as well
+    O4, _ = _run(k, v, [1.0], block_c=4)
+    assert abs(O4 - Of) < 1e-13
+
+
+def test_pin_per_tile_value_descale():
+    """Scores (0, -1), one key per tile and per scale block, V codes (1, 1) with value
+    descales (0.5, 3.0).  Tile 1: u = 256 -> p8 = 256, o = 0.5 * 256 = 128.  Tile 2
+    (m stays 0): u = 256 e^-1 = 94.176 -> p8 = 96, o = 128 + 3.0 * 96 = 416."""
+    O, L = _run([C_ZERO, C_MINUS_ONE], [C_ONE, C_ONE], [0.5, 3.0], block_c=1, scale_rows=1)
+    l = 256.0 * (1.0 + math.exp(-1.0))
+    assert abs(O - 416.0 / l) < 1e-13
+    assert abs(L - (math.log(l) - 8 * math.log(2.0))) < 1e-13
+    # one descale for both tiles (either one) gives a different O
+    for dv in (0.5, 3.0):
+        Ow, _ = _run([C_ZERO, C_MINUS_ONE], [C_ONE, C_ONE], [dv, dv], block_c=1, scale_rows=1)
+        assert abs(Ow - 416.0 / l) > 0.1
+
+
+def test_pin_key_descales_enter_before_the_max():
+    """K codes (1, 2) with key descales (1.0, 0.25): the scores are (1, 0.5), so key 0
+    holds the maximum although its code is the smaller one.  u = (256, 256 e^-0.5 =
+    155.27) -> p8 = (256, 160) (step 16 in [128, 256)), V = (1, -1)."""
+    O, L = fp8.forward(_codes([C_ONE]), _codes([C_ONE, C_TWO]), _codes([C_ONE, C_MINUS_ONE]), _descales([1.0]),
+                       _descales([1.0, 0.25]), _descales([1.0, 1.0]), 1.0, block_c=1, scale_rows=1)
+    l = 256.0 * (1.0 + math.exp(-0.5))
+    assert abs(float(O[0, 0, 0, 0]) - (256.0 - 160.0) / l) < 1e-13
+    assert abs(float(L[0, 0, 0]) - (1.0 + math.log(l) - 8 * math.log(2.0))) < 1e-13
 
 
 def test_quantised_output_is_close_to_dense_and_frames_differ_little():
