@@ -38,16 +38,16 @@ def test_quantize_matches_oracle(dtype, d, hadamard, per_tensor):
     back = fp8.decode(gc) * drow
     allowed = np.maximum(2 ** -4 * np.abs(xr), 2 ** -10 * drow) + 1e-5 * np.abs(xr).max()
     assert np.all(np.abs(back - xr) <= allowed)
-    if not hadamard:
-        # both sides form x / descale in float32 and round it to nearest even: exact
-        assert np.array_equal(gc, oc)
-    else:
-        # the transform itself is float32 on the GPU, float64 in the oracle: a code may
-        # differ only where the scaled value lies next to a rounding midpoint
-        u = np.abs(xr) / drow
-        alt = fp8.rounding_alternative(u, 1e-5)
-        assert np.all((gc == oc) | (np.abs(fp8.decode(gc)) == alt))
-        assert (gc == oc).mean() >= 0.999
+    # The oracle rounds the exact quotient x / descale once; the kernel rounds its
+    # float32 quotient (correctly rounded, so within 2^-24 relative of the exact one).
+    # The two roundings can differ only where the exact quotient lies that close to an
+    # E4M3 midpoint; the transform adds its own float32 error (the butterflies: 1e-5).
+    # There either neighbour is accepted, with the sign of x.
+    rel = 2.0 ** -23 if not hadamard else 1e-5
+    u = xr / drow
+    alt_code = fp8.encode_rne_sat(np.copysign(fp8.rounding_alternative(np.abs(u), rel), u))
+    assert np.all((gc == oc) | (gc == alt_code))
+    assert (gc == oc).mean() >= (0.9999 if not hadamard else 0.999)
 
 
 def test_incoherent_quantized_scores_stay_close():
