@@ -173,16 +173,39 @@ def fp8_kv_tile() -> int:
     return lib().attn_fp8_kv_tile()
 
 
+_FP8_CODE_DTYPES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale=None, o_dtype=torch.bfloat16,
-                 o=None, lse=None, stream=None):
+                 o=None, lse=None, stream=None, causal=False):
     """Forward on E4M3FN codes (uint8 or float8_e4m3fn tensors) with 128-row-block descales."""
+    # types first (TypeError), then shapes, layout and device (ValueError): nothing
+    # reaches the library unless every tensor is what the kernel will read or write
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.dtype not in _FP8_CODE_DTYPES:
+            raise TypeError(f"{n} must hold E4M3FN codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32, got {t.dtype}")
+    if o is not None and o.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"o must be bfloat16 or float32, got {o.dtype}")
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _require(t, n, 4)
     B, Hq, Sq, d = q8.shape
     Hkv, Sk = k8.shape[1], k8.shape[2]
+    dev = q8.device
+    _expect(k8, "k8", (B, Hkv, Sk, d), k8.dtype, dev)
+    _expect(v8, "v8", (B, Hkv, Sk, d), v8.dtype, dev)
+    _expect(q_scale, "q_scale", (B, Hq, (Sq + 127) // 128), torch.float32, dev)
+    _expect(k_scale, "k_scale", (B, Hkv, (Sk + 127) // 128), torch.float32, dev)
+    _expect(v_scale, "v_scale", (B, Hkv, (Sk + 127) // 128), torch.float32, dev)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty((B, Hq, Sq, d), dtype=o_dtype, device=q8.device) if o is None else o
-    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device) if lse is None else lse
+    o = torch.empty((B, Hq, Sq, d), dtype=o_dtype, device=dev) if o is None else o
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if lse is None else lse
+    _expect(o, "o", (B, Hq, Sq, d), o.dtype, dev)
+    _expect(lse, "lse", (B, Hq, Sq), torch.float32, dev)
     st = lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
-                            _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, scale, 0, _code(o.dtype),
+                            _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), _code(o.dtype),
                             _stream(stream))
     _lib.check("attn_fwd_fp8", st)
     return o, lse
@@ -258,16 +281,33 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=None, wo
                         o=None, lse=None, stream=None):
     """Split-KV decode: q [B,Hq,1,d], caches [B,Hkv,Smax,d], seqlens int32 [B] on device.
     chunk=None takes the library's choice (decode_pick_chunk)."""
+    _code(q.dtype)
+    if seqlens.dtype != torch.int32:
+        raise TypeError(f"seqlens must be int32, got {seqlens.dtype}")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{n} must have q's dtype {q.dtype}, got {t.dtype}")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n, 4)
     B, Hq, _, d = q.shape
     Hkv, Smax = k_cache.shape[1], k_cache.shape[2]
+    _expect(q, "q", (B, Hq, 1, d), q.dtype, q.device)
+    _expect(k_cache, "k_cache", (B, Hkv, Smax, d), q.dtype, q.device)
+    _expect(v_cache, "v_cache", (B, Hkv, Smax, d), q.dtype, q.device)
+    _expect(seqlens, "seqlens", (B,), torch.int32, q.device)
     if chunk is None:
         chunk = decode_pick_chunk(B, Hq, Smax)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, 1), torch.float32, q.device)
     need = decode_workspace_size(B, Hq, Smax, d, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require(workspace, "workspace", workspace.dim())
+    if workspace.device != q.device:
+        raise ValueError(f"workspace must be on {q.device}")
     st = lib().attn_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o), _ptr(lse),
                                    B, Hq, Hkv, Smax, d, scale, chunk, _code(q.dtype), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))

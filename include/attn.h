@@ -121,7 +121,6 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float
                      attn_dtype_t dtype, void* stream);
 
 /*
- * attn_fwd_varlen -- /*
  * attn_fwd_varlen -- the forward of attn_fwd on packed variable-length sequences.
  * "M4.4 - FlashAttention-2 Work Partitioning and the Decode Boundary", sections 0x04B
  * (a packed launch covers the longest sequence; workgroups past a sequence's rows

@@ -217,3 +217,30 @@ def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libattn.so"))
     with pytest.raises(_lib.LibraryMissing):
         _lib.lib()
+
+
+def test_fp8_and_decode_bindings_check_types_first():
+    """The Python bindings reject a wrong dtype (TypeError) and then a wrong shape,
+    layout or device (ValueError) before the library is called."""
+    import torch
+    import exact_tiled_attention_amd as eta
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    q8, k8 = u8(1, 2, 8, 128), u8(1, 2, 8, 128)
+    sc = f32(1, 2, 1)
+    with pytest.raises(TypeError):
+        eta.attn_fwd_fp8(q8.float(), k8, k8, sc, sc, sc)
+    with pytest.raises(TypeError):
+        eta.attn_fwd_fp8(q8, k8, k8, sc.double(), sc, sc)
+    with pytest.raises(TypeError):
+        eta.attn_fwd_fp8(q8, k8, k8, sc, sc, sc, o=torch.zeros(1, 2, 8, 128, dtype=torch.float16))
+    with pytest.raises(ValueError):                       # CPU tensors: not on a GPU
+        eta.attn_fwd_fp8(q8, k8, k8, sc, sc, sc)
+    q = torch.zeros(2, 8, 1, 128, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 2, 512, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        eta.attn_decode_splitkv(q, kc, kc, torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(TypeError):
+        eta.attn_decode_splitkv(q, kc.half(), kc, torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        eta.attn_decode_splitkv(q, kc, kc, torch.zeros(2, dtype=torch.int32))
