@@ -53,29 +53,45 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _time_launches(fn, steps, warmup, torch):
-    """Average launch duration (ms) over back-to-back launches between HIP events.
+def _time_launches(fn, steps, warmup, torch, min_samples=20):
+    """Device time per launch of ``fn`` on the current stream.
 
-    The timed region holds only the launches (no event between two launches), so the
-    host-side launch cost overlaps the previous kernel and the average is the device
-    time per launch.  It is split into up to five equal blocks, each bracketed by its
-    own events, for the spread.  Returns (block averages, region time)."""
+    ``warmup`` untimed launches, then two timed passes:
+      * region: exactly ``steps`` back-to-back launches between two HIP events (no event
+        between two launches, so the host's launch cost overlaps the previous kernel);
+        its mean is the throughput figure;
+      * samples: max(steps, min_samples) launches with an event after each one; the
+        intervals between consecutive events are the raw per-launch samples, whose
+        median is reported.
+    Returns a dict with ms_mean (region / steps), ms_median, the samples and counts."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    nblk = max(1, min(5, steps))
-    sizes = [steps // nblk + (1 if i < steps % nblk else 0) for i in range(nblk)]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nblk + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    region = e0.elapsed_time(e1)
+    n = max(steps, min_samples)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     torch.cuda.synchronize()
     evs[0].record(stream)
-    for i, n in enumerate(sizes):
-        for _ in range(n):
-            fn()
+    for i in range(n):
+        fn()
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) / n for i, n in enumerate(sizes)]
-    return per, evs[0].elapsed_time(evs[-1])
+    samples = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    return {"ms_mean": region / steps, "ms_median": statistics.median(samples), "samples_ms": samples,
+            "timed_launches": steps, "sampled_launches": n, "warmup_launches": warmup}
+
+
+def _timing_fields(t):
+    return {"ms_mean": t["ms_mean"], "ms_median": t["ms_median"], "timed_launches": t["timed_launches"],
+            "sampled_launches": t["sampled_launches"], "warmup_launches": t["warmup_launches"],
+            "samples_ms": [round(x, 5) for x in t["samples_ms"]]}
 
 
 def _fwd_flops(B, Hq, Sq, Sk, d, causal):
@@ -96,12 +112,11 @@ def bench_fwd(name, w, steps, warmup, torch, eta, dropout_p=None, exp_emulated=N
     else:
         fn = lambda: eta.attn_fwd_dropout(q, k, v, dropout_p, 1234, 0, scale=p["scale"], causal=p["causal"],
                                           o=o, lse=lse)
-    per, region = _time_launches(fn, steps, warmup, torch)
+    t_ = _time_launches(fn, steps, warmup, torch)
     flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
-    med = region / steps
-    return {"workload": name, "kernel": "fwd_kernel", "ms_median": med, "ms_region_per_step": region / steps,
-            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
-            "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}, (q, k, v, o, lse)
+    return {"workload": name, "kernel": "fwd_kernel", **_timing_fields(t_),
+            "tflops": flops / (t_["ms_mean"] * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
+            "peak": PEAK_TFLOPS[p["dtype"]]}, (q, k, v, o, lse)
 
 
 def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False, dropout_p=None):
@@ -120,34 +135,33 @@ def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False,
     fn = lambda: eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"],
                               grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv,
                               deterministic=deterministic, dropout_p=dropout_p, seed=1234, offset=0)
-    per, region = _time_launches(fn, steps, warmup, torch)
+    t_ = _time_launches(fn, steps, warmup, torch)
     flops = 2.5 * _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
-    med = region / steps
     kern = ("bwd deterministic (preprocess + column owner dK/dV + query owner dQ)" if deterministic
             else "bwd (preprocess + main + convert)")
-    return {"workload": name, "kernel": kern, "ms_median": med,
-            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
-            "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}
+    return {"workload": name, "kernel": kern, **_timing_fields(t_),
+            "tflops": flops / (t_["ms_mean"] * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
+            "peak": PEAK_TFLOPS[p["dtype"]]}
 
 
-def bench_decode(name, w, steps, warmup, torch, eta):
+def bench_decode(name, w, steps, warmup, torch, eta, chunk=None):
     t, p = w.tensors, w.params
     q, kc, vc = (t[n].cuda() for n in ("q", "k", "v"))
     lens = t["seqlens"].cuda()
-    chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["Smax"])
+    if chunk is None:
+        chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["Smax"])
     ws = torch.empty(eta.decode_workspace_size(p["B"], p["Hq"], p["Smax"], p["d"], chunk),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
     lse = torch.empty((p["B"], p["Hq"], 1), dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_decode_splitkv(q, kc, vc, lens, scale=p["scale"], chunk=chunk, workspace=ws,
                                          o=o, lse=lse)
-    per, region = _time_launches(fn, steps, warmup, torch)
+    t_ = _time_launches(fn, steps, warmup, torch)
     total_keys = int(t["seqlens"].sum())
     kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
-    med = region / steps
-    return {"workload": name + f", chunk {chunk}", "kernel": "decode split + merge", "ms_median": med,
-            "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
-            "chunk": chunk, "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
+    return {"workload": name + f", chunk {chunk}", "kernel": "decode split + merge", **_timing_fields(t_),
+            "gbs": kv_bytes / (t_["ms_mean"] * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
+            "chunk": chunk, "peak_gbs": PEAK_HBM_GBS}
 
 
 def bench_decode_paged(name, w, steps, warmup, torch, eta):
@@ -161,13 +175,12 @@ def bench_decode_paged(name, w, steps, warmup, torch, eta):
     lse = torch.empty((p["B"], p["Hq"], 1), dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_decode_paged(q, kp, vp, bt, lens, scale=p["scale"], chunk=chunk, workspace=ws,
                                        o=o, lse=lse)
-    per, region = _time_launches(fn, steps, warmup, torch)
+    t_ = _time_launches(fn, steps, warmup, torch)
     total_keys = int(t["seqlens"].sum())
     kv_bytes = total_keys * p["Hkv"] * p["d"] * 2 * 2
-    med = region / steps
-    return {"workload": name + f", chunk {chunk}", "kernel": "paged decode split + merge", "ms_median": med,
-            "gbs": kv_bytes / (med * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
-            "chunk": chunk, "page_size": p["page_size"], "peak_gbs": PEAK_HBM_GBS, "samples_ms": [round(x, 5) for x in per]}
+    return {"workload": name + f", chunk {chunk}", "kernel": "paged decode split + merge", **_timing_fields(t_),
+            "gbs": kv_bytes / (t_["ms_mean"] * 1e-3) / 1e9, "kv_bytes_per_call": kv_bytes, "sum_seqlen": total_keys,
+            "chunk": chunk, "page_size": p["page_size"], "peak_gbs": PEAK_HBM_GBS}
 
 
 def bench_fwd_varlen(name, w, steps, warmup, torch, eta):
@@ -177,13 +190,12 @@ def bench_fwd_varlen(name, w, steps, warmup, torch, eta):
     lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_fwd_varlen(q, k, v, cq, ck, p["max_seqlen_q"], p["max_seqlen_k"], scale=p["scale"],
                                      causal=p["causal"], o=o, lse=lse)
-    per, region = _time_launches(fn, steps, warmup, torch)
+    t_ = _time_launches(fn, steps, warmup, torch)
     sq, sk = p["seqlens_q"], p["seqlens_k"]
     flops = sum(_fwd_flops(1, p["Hq"], a, b, p["d"], p["causal"]) for a, b in zip(sq, sk))
-    med = region / steps
-    return {"workload": name, "kernel": "fwd_kernel (packed)", "ms_median": med,
-            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
-            "peak": PEAK_TFLOPS[p["dtype"]], "samples_ms": [round(x, 5) for x in per]}
+    return {"workload": name, "kernel": "fwd_kernel (packed)", **_timing_fields(t_),
+            "tflops": flops / (t_["ms_mean"] * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
+            "peak": PEAK_TFLOPS[p["dtype"]]}
 
 
 def bench_fp8(name, w, steps, warmup, torch, eta):
@@ -193,13 +205,12 @@ def bench_fp8(name, w, steps, warmup, torch, eta):
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, scale=p["scale"], o=o, lse=lse)
-    per, region = _time_launches(fn, steps, warmup, torch)
+    t_ = _time_launches(fn, steps, warmup, torch)
     flops = _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], False)
-    med = region / steps
-    return {"workload": name, "kernel": "fp8_fwd_kernel", "ms_median": med,
-            "tflops": flops / (med * 1e-3) / 1e12, "flops_per_call": flops, "dtype": "fp8_e4m3",
-            "peak": PEAK_TFLOPS["fp8"], "frac_of_bf16_peak": flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
-            "samples_ms": [round(x, 5) for x in per]}
+    tf = flops / (t_["ms_mean"] * 1e-3) / 1e12
+    return {"workload": name, "kernel": "fp8_fwd_kernel", **_timing_fields(t_),
+            "tflops": tf, "flops_per_call": flops, "dtype": "fp8_e4m3",
+            "peak": PEAK_TFLOPS["fp8"], "frac_of_bf16_peak": tf / PEAK_TFLOPS["bf16"]}
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -222,8 +233,91 @@ def cpu_baseline(w, budget_s=12.0):
     el = time.perf_counter() - t0
     flops = _fwd_flops(1, done, p["Sq"], p["Sk"], p["d"], p["causal"])
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "blas_threads": int(threads), "os_cpu_count": os.cpu_count(),
             "sample": f"{done} (batch, head) passes of the headline workload ({len(heads)} pairs per call), "
                       f"float64 numpy, {el:.1f} s"}
+
+
+def _guard(configs, key, fn, eta):
+    try:
+        configs[key] = fn()
+    except eta.AttnError as e:
+        configs[key] = {"error": str(e)}
+
+
+def run_extra(want, steps, warmup, torch, eta, attn_inputs):
+    """The secondary workloads, each timed over max(steps, 20) launches after `warmup`."""
+    n = max(steps, 20)
+    configs = {}
+    if "latency" in want:
+        _log("[bench] small forward latency")
+        w1 = attn_inputs.CONFIGS["fwd_f16_1x4x128_d64"]()
+        r, _ = bench_fwd("fp16 fwd q,k,v [1,4,128,64] non-causal (latency)", w1, n, warmup, torch, eta)
+        r["us_mean"], r["us_median"] = 1e3 * r["ms_mean"], 1e3 * r["ms_median"]
+        configs["small_fwd_latency"] = r
+    if "exp_emulated" in want:
+        w2 = attn_inputs.CONFIGS["fwd_f16_1x8x4096_d64"]()
+        for emu in (2, 4):
+            _log(f"[bench] headline with {emu} of 8 exponentials in software")
+            r, _ = bench_fwd(HEAD_NAME + f", {emu}/8 exponentials by software exp2", w2, n, warmup, torch, eta,
+                             exp_emulated=emu)
+            configs[f"fwd_exp_emulated_{emu}"] = r
+    if "causal_gqa" in want:
+        _log("[bench] causal GQA prefill fwd + bwd")
+        w3 = attn_inputs.CONFIGS["causal_gqa_bf16_2x32x8192_kv8_d128"]()
+        name = "bf16 causal GQA q [2,32,8192,128] k,v [2,8,8192,128]"
+        r, bufs = bench_fwd(name + " fwd", w3, n, warmup, torch, eta)
+        configs["causal_gqa_fwd"] = r
+        _guard(configs, "causal_gqa_bwd", lambda: bench_bwd(name + " bwd", w3, bufs, n, warmup, torch, eta), eta)
+        _guard(configs, "causal_gqa_bwd_deterministic",
+               lambda: bench_bwd(name + " bwd, deterministic", w3, bufs, n, warmup, torch, eta,
+                                 deterministic=True), eta)
+        try:
+            r, dbufs = bench_fwd(name + " fwd, dropout 0.1", w3, n, warmup, torch, eta, dropout_p=0.1)
+            configs["causal_gqa_fwd_dropout"] = r
+            configs["causal_gqa_bwd_dropout"] = bench_bwd(name + " bwd, dropout 0.1", w3, dbufs, n, warmup,
+                                                          torch, eta, dropout_p=0.1)
+            del dbufs
+        except eta.AttnError as e:
+            configs["causal_gqa_fwd_dropout"] = {"error": str(e)}
+        del bufs, w3
+        torch.cuda.empty_cache()
+        _log("[bench] packed variable-length prefill fwd")
+        lens = attn_inputs.decode_lengths(3, 8, 256, 4096).tolist()
+        w3v = attn_inputs.varlen_prefill(lens, lens, 32, 8, 128, "bf16", seed=3, causal=True)
+        _guard(configs, "causal_gqa_fwd_varlen", lambda: bench_fwd_varlen(
+            f"bf16 causal GQA packed Hq=32 Hkv=8 d=128, 8 sequences S~U[256,4096] (total {sum(lens)})",
+            w3v, n, warmup, torch, eta), eta)
+        del w3v
+        torch.cuda.empty_cache()
+    if "decode" in want:
+        _log("[bench] split-KV decode")
+        w4 = attn_inputs.CONFIGS["decode_bf16_b64_hq32_kv8_d128"]()
+        dname = "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768]"
+        # the workload as written (256-token chunks), then the library's own chunk choice
+        _guard(configs, "decode_chunk256", lambda: bench_decode(dname, w4, n, warmup, torch, eta, chunk=256), eta)
+        _guard(configs, "decode", lambda: bench_decode(dname, w4, n, warmup, torch, eta), eta)
+        del w4
+        torch.cuda.empty_cache()
+        _log("[bench] paged split-KV decode")
+        w4p = attn_inputs.paged_decode(64, 32, 8, 128, "bf16", seed=4, page_size=128)
+        _guard(configs, "decode_paged", lambda: bench_decode_paged(
+            "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768], paged pool P=128, permuted block table",
+            w4p, n, warmup, torch, eta), eta)
+        del w4p
+        torch.cuda.empty_cache()
+    if "fp8" in want:
+        _log("[bench] fp8 forward")
+        w5 = attn_inputs.CONFIGS["fwd_fp8_4x16x8192_d128"]()
+        _guard(configs, "fp8_fwd", lambda: bench_fp8("fp8 e4m3 fwd [4,16,8192,128] 128-row block scales, bf16 out",
+                                                     w5, n, warmup, torch, eta), eta)
+        del w5
+        torch.cuda.empty_cache()
+    return configs
+
+
+HEAD_NAME = "fp16 fwd q,k,v [1,8,4096,64] non-causal"
+EXTRA = ["latency", "exp_emulated", "causal_gqa", "decode", "fp8"]
 
 
 def main():
@@ -231,7 +325,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--only", default=None, help="run only this extra workload (exp_emulated, causal_gqa, decode, fp8)")
+    ap.add_argument("--only", default=None, help="run only this extra workload (" + ", ".join(EXTRA) + ")")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -241,6 +335,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the kernels run on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -258,88 +355,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    head_name = "fp16 fwd q,k,v [1,8,4096,64] non-causal"
-    w2 = attn_inputs.CONFIGS["fwd_f16_1x8x4096_d64"]()
-    _log("[bench] headline", head_name)
-    head, _ = bench_fwd(head_name, w2, args.steps, args.warmup, torch, eta)
-
+    # The secondary workloads run first and the headline last, so that the headline's
+    # W warm-up and K timed launches run on a GPU already at its working clocks.
     configs = {}
     if not args.no_extra:
-        want = [args.only] if args.only else ["exp_emulated", "causal_gqa", "decode", "fp8"]
-        if "exp_emulated" in want:
-            for emu in (2, 4):
-                _log(f"[bench] headline with {emu} of 8 exponentials in software")
-                r, _ = bench_fwd(head_name + f", {emu}/8 exponentials by software exp2", w2, args.steps,
-                                 args.warmup, torch, eta, exp_emulated=emu)
-                configs[f"fwd_exp_emulated_{emu}"] = r
-        if "causal_gqa" in want:
-            _log("[bench] causal GQA prefill fwd + bwd")
-            w3 = attn_inputs.CONFIGS["causal_gqa_bf16_2x32x8192_kv8_d128"]()
-            name = "bf16 causal GQA q [2,32,8192,128] k,v [2,8,8192,128]"
-            r, bufs = bench_fwd(name + " fwd", w3, max(5, args.steps // 3), 2, torch, eta)
-            configs["causal_gqa_fwd"] = r
-            try:
-                configs["causal_gqa_bwd"] = bench_bwd(name + " bwd", w3, bufs, max(3, args.steps // 5), 1, torch, eta)
-            except eta.AttnError as e:
-                configs["causal_gqa_bwd"] = {"error": str(e)}
-            try:
-                configs["causal_gqa_bwd_deterministic"] = bench_bwd(name + " bwd, deterministic", w3, bufs,
-                                                            max(3, args.steps // 5), 1, torch, eta,
-                                                            deterministic=True)
-            except eta.AttnError as e:
-                configs["causal_gqa_bwd_deterministic"] = {"error": str(e)}
-            try:
-                r, dbufs = bench_fwd(name + " fwd, dropout 0.1", w3, max(5, args.steps // 3), 2, torch, eta,
-                                     dropout_p=0.1)
-                configs["causal_gqa_fwd_dropout"] = r
-                configs["causal_gqa_bwd_dropout"] = bench_bwd(name + " bwd, dropout 0.1", w3, dbufs,
-                                                      max(3, args.steps // 5), 1, torch, eta, dropout_p=0.1)
-                del dbufs
-            except eta.AttnError as e:
-                configs["causal_gqa_fwd_dropout"] = {"error": str(e)}
-            del bufs, w3
-            torch.cuda.empty_cache()
-            _log("[bench] packed variable-length prefill fwd")
-            lens = attn_inputs.decode_lengths(3, 8, 256, 4096).tolist()
-            w3v = attn_inputs.varlen_prefill(lens, lens, 32, 8, 128, "bf16", seed=3, causal=True)
-            try:
-                configs["causal_gqa_fwd_varlen"] = bench_fwd_varlen(
-                    f"bf16 causal GQA packed Hq=32 Hkv=8 d=128, 8 sequences S~U[256,4096] (total {sum(lens)})",
-                    w3v, max(5, args.steps // 3), 2, torch, eta)
-            except eta.AttnError as e:
-                configs["causal_gqa_fwd_varlen"] = {"error": str(e)}
-            del w3v
-            torch.cuda.empty_cache()
-        if "decode" in want:
-            _log("[bench] split-KV decode")
-            w4 = attn_inputs.CONFIGS["decode_bf16_b64_hq32_kv8_d128"]()
-            try:
-                configs["decode"] = bench_decode("bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768]",
-                                                    w4, args.steps, args.warmup, torch, eta)
-            except eta.AttnError as e:
-                configs["decode"] = {"error": str(e)}
-            del w4
-            torch.cuda.empty_cache()
-            _log("[bench] paged split-KV decode")
-            w4p = attn_inputs.paged_decode(64, 32, 8, 128, "bf16", seed=4, page_size=128)
-            try:
-                configs["decode_paged"] = bench_decode_paged(
-                    "bf16 GQA decode B=64 Hq=32 Hkv=8 d=128 Sk~U[1024,32768], paged pool P=128, "
-                    "permuted block table", w4p, args.steps, args.warmup, torch, eta)
-            except eta.AttnError as e:
-                configs["decode_paged"] = {"error": str(e)}
-            del w4p
-            torch.cuda.empty_cache()
-        if "fp8" in want:
-            _log("[bench] fp8 forward")
-            w5 = attn_inputs.CONFIGS["fwd_fp8_4x16x8192_d128"]()
-            try:
-                configs["fp8_fwd"] = bench_fp8("fp8 e4m3 fwd [4,16,8192,128] 128-row block scales, bf16 out",
-                                              w5, max(5, args.steps // 3), 2, torch, eta)
-            except eta.AttnError as e:
-                configs["fp8_fwd"] = {"error": str(e)}
-            del w5
-            torch.cuda.empty_cache()
+        want = [args.only] if args.only else EXTRA
+        configs = run_extra(want, args.steps, args.warmup, torch, eta, attn_inputs)
+
+    w2 = attn_inputs.CONFIGS["fwd_f16_1x8x4096_d64"]()
+    _log("[bench] headline", HEAD_NAME)
+    head, _ = bench_fwd(HEAD_NAME, w2, args.steps, args.warmup, torch, eta)
 
     cpu = None
     if not args.no_cpu:
@@ -354,17 +379,18 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["ms_region_per_step"], 5),
+        "ms_per_step": round(head["ms_mean"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": head_name, "B": 1, "H": 8, "S": 4096, "d": 64, "causal": False,
+        "config": {"workload": HEAD_NAME, "B": 1, "H": 8, "S": 4096, "d": 64, "causal": False,
                    "flops_per_step": head["flops_per_call"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f16"], 4), "traffic": measured_traffic(),
-                     "kernel": "fwd_kernel", "kernel_ms_median": round(head["ms_median"], 5)},
+                     "kernel": "fwd_kernel", "kernel_ms_mean": round(head["ms_mean"], 5),
+                     "kernel_ms_median": round(head["ms_median"], 5)},
         "cpu_baseline": cpu,
         "configs": {k: {kk: vv for kk, vv in v.items() if kk != "samples_ms"} for k, v in configs.items()},
         "samples_ms": head["samples_ms"],
