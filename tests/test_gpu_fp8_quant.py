@@ -47,9 +47,12 @@ def test_quantize_matches_oracle(dtype, d, hadamard, per_tensor):
     u = xr / drow
     alt_code = fp8.encode_rne_sat(np.copysign(fp8.rounding_alternative(np.abs(u), rel), u))
     assert np.all((gc == oc) | (gc == alt_code))
-    # (ambiguous quotients are not rare here: with 11-bit inputs, 448 x / amax often is
-    # exactly an E4M3 midpoint, and the rounded descale then decides the side)
-    assert (gc == oc).mean() >= 0.999
+    # (ambiguous quotients are not rare here: with 8- or 11-bit inputs, 448 x / amax is
+    # often exactly an E4M3 midpoint, and the rounded descale then decides the side;
+    # the bound below only guards against a systematic error)
+    same = float((gc == oc).mean())
+    say(f"    identical codes: {same:.5f}")
+    assert same >= 0.99
 
 
 def test_incoherent_quantized_scores_stay_close():
