@@ -102,6 +102,10 @@ __global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
+  // bf16 dropout (training): the probabilities enter P V as a two-term bf16 sum hi + lo
+  // (~16 significant bits), so the stored O is the rounding of an O accurate to fp32
+  // level and the backward's D = rowsum(dO o O) sees only that storage rounding
+  constexpr bool SPLIT = DROP && std::is_same<T, bf16>::value;
   constexpr int BC = QB == 2 ? 32 : 64;       // keys per K/V tile
   typedef Tile<D, BC> TL;
   constexpr int BQ = RW * QB * 32;            // query rows per workgroup
@@ -297,7 +301,7 @@ void fwd_kernel(FwdArgs a) {
   // addresses key row s/4, d columns 4(s%4) .. +3.
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-  auto pv_chunk = [&](const u32x4 (&p)[QB], int slot, int cc) {
+  auto pv_chunk = [&](const u32x4 (&p)[QB], const u32x4 (&plo)[QB], int slot, int cc) {
     const uint8_t* vs = vring + slot * TL::BYTES;
     const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
     const int r1 = r0 + 8;
@@ -314,7 +318,10 @@ void fwd_kernel(FwdArgs a) {
       const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
       const u32x4 av4 = {l2.x, l2.y, h2.x, h2.y};
 #pragma unroll
-      for (int j = 0; j < QB; ++j) o[j][db] = E::mfma(as_v8<V8>(av4), as_v8<V8>(p[j]), o[j][db]);
+      for (int j = 0; j < QB; ++j) {
+        o[j][db] = E::mfma(as_v8<V8>(av4), as_v8<V8>(p[j]), o[j][db]);
+        if constexpr (SPLIT) o[j][db] = E::mfma(as_v8<V8>(av4), as_v8<V8>(plo[j]), o[j][db]);
+      }
     }
   };
 
@@ -327,7 +334,7 @@ void fwd_kernel(FwdArgs a) {
   // 1 / (1 - p).  Registers 4q .. 4q+3 of a key block are 4 consecutive keys, so one
   // Philox call (counter (key / 4, query row, b H_q + h, offset)) decides all four.
   auto probs_chunk = [&](const f32x16 (&sc)[KB], int cc, float m_use, float& l0, float& l1, int t,
-                         int j) -> u32x4 {
+                         int j, u32x4& lo) -> u32x4 {
     const int kbk = cc >> 1;
     const int hb = (cc & 1) * 8;
     u32x4 w0 = {}, w1 = {};
@@ -337,7 +344,7 @@ void fwd_kernel(FwdArgs a) {
       w0 = philox4x32_10(grp4, (uint32_t)qrow[j], bhq, a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
       w1 = philox4x32_10(grp4 + 2, (uint32_t)qrow[j], bhq, a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
     }
-    uint32_t pk[4];
+    uint32_t pk[4], pl[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const float e0 = fast_exp2(fmaf(sc[kbk][hb + 2 * jj], c, -m_use));
@@ -350,10 +357,15 @@ void fwd_kernel(FwdArgs a) {
         const float k0 = wv[2 * (jj & 1)] >= a.drop.thresh ? e0 : 0.f;
         const float k1 = wv[2 * (jj & 1) + 1] >= a.drop.thresh ? e1 : 0.f;
         pk[jj] = E::pack2(k0, k1);
+        if constexpr (SPLIT) {
+          // remainders after the bf16 rounding (bf16 -> f32 is a 16-bit shift)
+          pl[jj] = E::pack2(k0 - __uint_as_float(pk[jj] << 16), k1 - __uint_as_float(pk[jj] & 0xFFFF0000u));
+        }
       } else {
         pk[jj] = E::pack2(e0, e1);
       }
     }
+    lo = u32x4{pl[0], pl[1], pl[2], pl[3]};
     return u32x4{pk[0], pk[1], pk[2], pk[3]};
   };
 
@@ -476,25 +488,25 @@ void fwd_kernel(FwdArgs a) {
       l0[j] = 0.f;
       l1[j] = 0.f;
     }
-    auto probs = [&](int cc, u32x4 (&p)[QB]) {
+    auto probs = [&](int cc, u32x4 (&p)[QB], u32x4 (&plo)[QB]) {
 #pragma unroll
-      for (int j = 0; j < QB; ++j) p[j] = probs_chunk(cur[j], cc, m_use[j], l0[j], l1[j], t, j);
+      for (int j = 0; j < QB; ++j) p[j] = probs_chunk(cur[j], cc, m_use[j], l0[j], l1[j], t, j, plo[j]);
     };
     if (has_cur && has_nxt) {
       // steady state: one basic block, chunk by chunk
 #pragma unroll
       for (int cc = 0; cc < PC; ++cc) {
         score_part(nxt, (i + 1) % DEPTH, cc * KPC, (cc + 1) * KPC);
-        u32x4 p[QB];
-        probs(cc, p);
-        pv_chunk(p, i % DEPTH, cc);
+        u32x4 p[QB], plo[QB];
+        probs(cc, p, plo);
+        pv_chunk(p, plo, i % DEPTH, cc);
       }
     } else if (has_cur) {
 #pragma unroll
       for (int cc = 0; cc < PC; ++cc) {
-        u32x4 p[QB];
-        probs(cc, p);
-        pv_chunk(p, i % DEPTH, cc);
+        u32x4 p[QB], plo[QB];
+        probs(cc, p, plo);
+        pv_chunk(p, plo, i % DEPTH, cc);
       }
     } else if (has_nxt) {
       score_part(nxt, (i + 1) % DEPTH, 0, KC);

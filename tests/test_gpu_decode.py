@@ -49,15 +49,19 @@ def test_decode_long_chunk_and_uneven_lengths(chunk):
     _run(w, chunk)
 
 
-def test_decode_b64_full_size_sampled():
+@pytest.mark.parametrize("chunk", [256, None])
+def test_decode_b64_full_size_sampled(chunk):
+    """The full-size workload in both benchmarked launches: 256-token chunks as the
+    workload is written, and the library's own pick (1536 keys)."""
     need_gpu()
     w = attn_inputs.CONFIGS["decode_bf16_b64_hq32_kv8_d128"]()
     lens = w.tensors["seqlens"].numpy()
     pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 42, 63})
     import exact_tiled_attention_amd as eta
     p = w.params
-    chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["Smax"])   # the benchmarked launch
-    assert chunk == 1536
+    if chunk is None:
+        chunk = eta.decode_pick_chunk(p["B"], p["Hq"], p["Smax"])
+        assert chunk == 1536
     _run(w, chunk, batches=pick)
 
 

@@ -63,14 +63,25 @@ def test_dropout_forward_elementwise(dtype, d, causal, B, Hq, Hkv, Sq, Sk, p):
     say(f"    max|dO|={e1:.2e} max|dLSE|={e2:.2e}")
 
 
-def test_dropout_zero_rate_is_the_plain_forward_and_repeatable():
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_dropout_zero_rate_is_the_plain_forward_and_repeatable(dtype):
+    """p = 0 keeps everything: fp16 gives the plain forward bit for bit; bf16 carries the
+    probabilities into P V as hi + lo bf16 pairs in the dropout forward, so its O is the
+    more accurate one (same LSE, O within the bf16 tolerance of the plain forward's)."""
     need_gpu()
     import exact_tiled_attention_amd as eta
-    w = attn_inputs.prefill(1, 8, 2, 333, 333, 128, "bf16", seed=81, causal=True)
+    w = attn_inputs.prefill(1, 8, 2, 333, 333, 128, dtype, seed=81, causal=True)
     q, k, v = (to_dev(w.tensors[n]) for n in ("q", "k", "v"))
     o0, l0 = eta.attn_fwd(q, k, v, causal=True)
     o1, l1 = eta.attn_fwd_dropout(q, k, v, 0.0, 5, 0, causal=True)
-    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(l0, l1)
+    if dtype == "f16":
+        assert torch.equal(o0, o1)
+    else:
+        O, _ = dense.forward(w.tensors["q"], w.tensors["k"], w.tensors["v"], w.params["scale"], True)
+        e_plain = assert_close_out(o0.cpu(), O, TOL_OUT[torch.bfloat16], "plain")
+        e_split = assert_close_out(o1.cpu(), O, TOL_OUT[torch.bfloat16], "dropout p=0")
+        say(f"    bf16 max err: plain {e_plain:.2e}, dropout p=0 {e_split:.2e}")
     a, la = eta.attn_fwd_dropout(q, k, v, 0.2, 5, 7, causal=True)
     b, lb = eta.attn_fwd_dropout(q, k, v, 0.2, 5, 7, causal=True)
     c, _ = eta.attn_fwd_dropout(q, k, v, 0.2, 5, 8, causal=True)
@@ -125,3 +136,33 @@ def test_dropout_backward_deterministic_repeatable_and_split():
     ref = dropout.backward(t["q"], t["k"], t["v"], t["do"], prm["scale"], True, 0.3, 77, 5, o_storage=t["q"].dtype)
     for g_, r_ in zip(a, ref):
         assert_close_out(g_, r_, TOL_GRAD, w.name)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,p", [
+    (1, 4, 2, 257, 193, 0.15),     # query and key tails, GQA 2
+    (1, 2, 2, 300, 100, 0.4),      # causal rows with few or no visible keys
+    (2, 8, 2, 200, 333, 0.25),     # S_q < S_k, GQA 4
+])
+def test_dropout_training_chain_end_to_end(deterministic, dtype, d, causal, B, Hq, Hkv, Sq, Sk, p):
+    """attn_fwd_dropout, then attn_bwd with the same dropout_p, seed and offset on the
+    forward's own O and LSE, against the oracle's exact gradients (D from the oracle's
+    O rounded to the element type, as a forward stores it)."""
+    need_gpu()
+    import exact_tiled_attention_amd as eta
+    w = attn_inputs.prefill(B, Hq, Hkv, Sq, Sk, d, dtype, seed=950 + Sq + d, causal=causal, with_grad=True)
+    t, prm = w.tensors, w.params
+    seed, offset = 9090 + Sk, 4
+    say(f"[dropout-chain] {w.name} causal={causal} p={p} det={deterministic}")
+    q, k, v, do = (to_dev(t[n]) for n in ("q", "k", "v", "do"))
+    o, lse = eta.attn_fwd_dropout(q, k, v, p, seed, offset, scale=prm["scale"], causal=causal)
+    g = eta.attn_bwd(q, k, v, o, lse, do, scale=prm["scale"], causal=causal, dropout_p=p, seed=seed,
+                     offset=offset, deterministic=deterministic)
+    torch.cuda.synchronize()
+    ref = dropout.backward(t["q"], t["k"], t["v"], t["do"], prm["scale"], causal, p, seed, offset,
+                           o_storage=t["q"].dtype)
+    errs = [assert_close_out(g_.cpu(), r_, TOL_GRAD, f"{w.name} {n}") for n, g_, r_ in zip(("dq", "dk", "dv"), g, ref)]
+    say("    max err dq/dk/dv = " + " ".join(f"{e:.2e}" for e in errs))
