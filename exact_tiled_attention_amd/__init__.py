@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_exp_emulated", "exp2_soft", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv",
+__all__ = ["attn_fwd", "attn_fwd_exp_emulated", "exp2_soft", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -312,6 +312,42 @@ def attn_decode_splitkv(q, k_cache, v_cache, seqlens, scale=None, chunk=None, wo
                                    B, Hq, Hkv, Smax, d, scale, chunk, _code(q.dtype), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("attn_decode_splitkv", st)
+    return o, lse
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attn_decode_splitkv_noalloc(q, k_cache, v_cache, seqlens, scale=None, chunk=None, o=None, lse=None,
+                                stream=None):
+    """attn_decode_splitkv with the partial states in the library's own per-GPU device
+    scratch (no workspace; the library call allocates nothing).  o and lse must be
+    given by callers that cannot allocate; chunk=None takes the library's choice."""
+    _code(q.dtype)
+    if seqlens.dtype != torch.int32:
+        raise TypeError(f"seqlens must be int32, got {seqlens.dtype}")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{n} must have q's dtype {q.dtype}, got {t.dtype}")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n, 4)
+    B, Hq, _, d = q.shape
+    Hkv, Smax = k_cache.shape[1], k_cache.shape[2]
+    _expect(q, "q", (B, Hq, 1, d), q.dtype, q.device)
+    _expect(k_cache, "k_cache", (B, Hkv, Smax, d), q.dtype, q.device)
+    _expect(v_cache, "v_cache", (B, Hkv, Smax, d), q.dtype, q.device)
+    _expect(seqlens, "seqlens", (B,), torch.int32, q.device)
+    if chunk is None:
+        chunk = decode_pick_chunk(B, Hq, Smax)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, 1), torch.float32, q.device)
+    st = lib().attn_decode_splitkv_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
+                                           _ptr(lse), B, Hq, Hkv, Smax, d, scale, chunk, _code(q.dtype),
+                                           _stream(stream))
+    _lib.check("attn_decode_splitkv_noalloc", st)
     return o, lse
 
 

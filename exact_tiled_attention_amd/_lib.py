@@ -42,6 +42,7 @@ PROTOTYPES = {
     "attn_decode_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode_pick_chunk": (_I, [_I, _I, _I]),
     "attn_decode_splitkv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
+    "attn_decode_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S, _P]),
     "attn_tile_plan": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
 }

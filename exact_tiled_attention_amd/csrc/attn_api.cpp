@@ -369,11 +369,13 @@ size_t attn_decode_workspace_size(int B, int Hq, int Smax, int d, int chunk) {
   return align256(parts * 2 * sizeof(float)) + align256(parts * d * sizeof(float));
 }
 
-int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
-                        const int* seqlens_k, void* o, float* lse,
-                        int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
-                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the contiguous-cache decode (pure host arithmetic).
+int check_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k, void* o,
+                 int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk, attn_dtype_t dtype) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || seqlens_k == nullptr ||
       o == nullptr)
     return ATTN_ERR_NULL;
@@ -382,6 +384,20 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (chunk <= 0 || chunk % 64 != 0 || chunk > 4096 || !isfinite(scale)) return ATTN_ERR_ARG;
   if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;   // one grid row per (b, kv head)
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                        const int* seqlens_k, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
+                        attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const int st = check_decode(q, k_cache, v_cache, seqlens_k, o, B, Hq, Hkv, Smax, d, scale, chunk, dtype);
+  if (st != ATTN_OK) return st;
   const size_t need = attn_decode_workspace_size(B, Hq, Smax, d, chunk);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   DecodeArgs a = {};
@@ -395,6 +411,21 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
   a.dtype_bf16 = dtype == ATTN_BF16;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(attn_launch_decode(a, (hipStream_t)stream));
+}
+
+int attn_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int* seqlens_k, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
+                                attn_dtype_t dtype, void* stream) {
+  const int st = check_decode(q, k_cache, v_cache, seqlens_k, o, B, Hq, Hkv, Smax, d, scale, chunk, dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = attn_decode_workspace_size(B, Hq, Smax, d, chunk);
+  if (need == 0 || need > (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (attn_decode_scratch(&ws) != hipSuccess) return ATTN_ERR_HIP;
+  // the split pass writes every partial the merge reads: nothing needs clearing
+  return attn_decode_splitkv(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Smax, d, scale, chunk, dtype,
+                             ws, need, stream);
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -27,6 +27,16 @@
 // max frame, O = u / l, LSE = m + ln l (all in base 2 internally).
 #include "attn_device.h"
 #include "attn_launch.h"
+#include "../../include/attn.h"
+
+#include <mutex>
+
+// Partial states of attn_decode_splitkv_noalloc, for callers that cannot allocate: a
+// file-scope device array (one copy per GPU the library runs on, alive until the
+// process ends).  Host code never passes `scratch` itself to a kernel (on the host the
+// name is only a stand-in); it uses the device address that attn_decode_scratch()
+// looks up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -380,4 +390,26 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 hipError_t attn_launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype_bf16) return launch_t<bf16>(a, stream);
   return launch_t<f16>(a, stream);
+}
+
+// Device address of this GPU's `scratch` (the current device), looked up on the first
+// call per device and kept; later calls return the kept address.
+hipError_t attn_decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }

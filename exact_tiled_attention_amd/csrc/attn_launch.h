@@ -112,3 +112,5 @@ hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int attn_fp8_tile_keys();
 hipError_t attn_launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t attn_launch_decode(const DecodeArgs& a, hipStream_t stream);
+// device address of the current GPU's decode scratch (ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+hipError_t attn_decode_scratch(void** ptr);

@@ -11,7 +11,8 @@
  * Conventions shared by every call
  *   - Tensors are contiguous row-major [B, H, S, d] ("BHSD") in device memory owned
  *     by the caller.  The library never allocates or frees device memory: scratch is
- *     passed in as a workspace whose size the matching *_workspace_size() returns.
+ *     passed in as a workspace whose size the matching *_workspace_size() returns
+ *     (attn_decode_splitkv_noalloc uses a fixed library-owned device array instead).
  *   - Query head h reads K/V head h / (H_q / H_kv); H_q must be a multiple of H_kv
  *     (M4.4, section 0x06A).  Output and LSE are indexed by query head.
  *   - causal != 0 makes cell (i, k) visible iff k <= i + (S_k - S_q), the bottom-right
@@ -24,7 +25,8 @@
  *     negative status without touching the GPU when they are invalid.  Valid calls
  *     are asynchronous on `stream` (a hipStream_t; NULL = the default stream); the
  *     results are ready after the stream is synchronised.  A failed launch returns
- *     ATTN_ERR_HIP.  The library keeps no state between calls.
+ *     ATTN_ERR_HIP.  The library keeps no state between calls (except the per-GPU
+ *     scratch of attn_decode_splitkv_noalloc).
  *   - Sizes are int (each dimension and each product used for indexing must fit the
  *     64-bit offsets the kernels use; S_q, S_k <= 2^20, B*H <= 2^16 are enforced).
  */
@@ -292,6 +294,29 @@ int attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                         int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
                         attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * attn_decode_splitkv_noalloc -- attn_decode_splitkv without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The partial states go to a
+ * library-owned device array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES per GPU (created
+ * when the library's code object is loaded on that GPU, kept until the process
+ * ends); the call itself allocates and frees nothing.  Its device address is looked
+ * up once per GPU on the first call there.
+ *
+ *   Arguments as attn_decode_splitkv without workspace / workspace_bytes.
+ *   ATTN_ERR_WORKSPACE when attn_decode_workspace_size(B, Hq, Smax, d, chunk) exceeds
+ *   ATTN_DECODE_NOALLOC_SCRATCH_BYTES (a larger chunk needs fewer partials).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ *   (several streams or host threads at once) race and must be serialised by the
+ *   caller.  The array keeps the last call's partials; nothing in it needs to start
+ *   at zero, since the split pass writes every partial the merge pass reads.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_decode_splitkv_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int* seqlens_k, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Smax, int d, float scale, int chunk,
+                                attn_dtype_t dtype, void* stream);
 
 /*
  * attn_decode_paged -- attn_decode_splitkv over a paged K/V pool.

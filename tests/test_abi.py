@@ -244,3 +244,17 @@ def test_fp8_and_decode_bindings_check_types_first():
         eta.attn_decode_splitkv(q, kc.half(), kc, torch.zeros(2, dtype=torch.int32))
     with pytest.raises(ValueError):
         eta.attn_decode_splitkv(q, kc, kc, torch.zeros(2, dtype=torch.int32))
+
+
+def test_decode_noalloc_checks_run_before_any_hip_call():
+    lib, _ = _lib()
+    def call(chunk=256, **kw):
+        a = dict(B=2, Hq=8, Hkv=2, Smax=512, d=128)
+        a.update(kw)
+        return lib.attn_decode_splitkv_noalloc(P, P, P, P, P, None, a["B"], a["Hq"], a["Hkv"], a["Smax"], a["d"],
+                                               0.088, chunk, 1, None)
+    assert call(chunk=100) == -8 and call(Hkv=3) == -3 and call(d=80) == -4 and call(Smax=0) == -2
+    # partial states past the 64 MiB device scratch: rejected on the host
+    assert lib.attn_decode_workspace_size(64, 32, 32768, 128, 256) > (64 << 20)
+    assert call(B=64, Hq=32, Hkv=8, Smax=32768, chunk=256) == -6
+    assert lib.attn_decode_splitkv_noalloc(None, P, P, P, P, None, 2, 8, 2, 512, 128, 0.088, 256, 1, None) == -1
