@@ -5,7 +5,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--only CONFIG] [--no-cpu] [
 A step is one call of the hot path on the headline workload, fp16 forward
 q,k,v [1,8,4096,64] non-causal (34.36 GFLOP per call).  Inputs are resident in HBM
 before the timed region; the region is bracketed by device synchronisation and
-timed with HIP events recorded on the stream the kernels are launched on.  The
+timed with HIP events recorded on the stream the kernels are launched on.  Each
+workload first runs about 0.2 s of untimed launches (clock settling), then the W
+warm-up launches, then exactly K timed launches (the secondary workloads at least
+20), then a second pass with an event after each launch for the raw samples.  The
 other workloads (the headline with 2 or 4 of every 8 softmax exponentials evaluated
 by the software exp2, causal GQA prefill forward + backward, split-KV decode, fp8
 forward) are timed the same way and reported under "configs".
@@ -53,10 +56,28 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+SETTLE_S = 0.2
+
+
+def _settle(fn, torch, seconds=SETTLE_S):
+    """Untimed launches of ``fn`` for about ``seconds`` of wall time, so that the GPU runs
+    at its working clock when the warm-up and the timed launches start (after the host
+    work between workloads the first launches run at a lower clock)."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
 def _time_launches(fn, steps, warmup, torch, min_samples=20):
     """Device time per launch of ``fn`` on the current stream.
 
-    ``warmup`` untimed launches, then two timed passes:
+    About SETTLE_S seconds of untimed launches (clock settling), ``warmup`` untimed
+    launches, then two timed passes:
       * region: exactly ``steps`` back-to-back launches between two HIP events (no event
         between two launches, so the host's launch cost overlaps the previous kernel);
         its mean is the throughput figure;
@@ -64,6 +85,7 @@ def _time_launches(fn, steps, warmup, torch, min_samples=20):
         intervals between consecutive events are the raw per-launch samples, whose
         median is reported.
     Returns a dict with ms_mean (region / steps), ms_median, the samples and counts."""
+    settle = _settle(fn, torch)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -85,12 +107,13 @@ def _time_launches(fn, steps, warmup, torch, min_samples=20):
     torch.cuda.synchronize()
     samples = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
     return {"ms_mean": region / steps, "ms_median": statistics.median(samples), "samples_ms": samples,
-            "timed_launches": steps, "sampled_launches": n, "warmup_launches": warmup}
+            "timed_launches": steps, "sampled_launches": n, "warmup_launches": warmup, "settle_launches": settle}
 
 
 def _timing_fields(t):
     return {"ms_mean": t["ms_mean"], "ms_median": t["ms_median"], "timed_launches": t["timed_launches"],
             "sampled_launches": t["sampled_launches"], "warmup_launches": t["warmup_launches"],
+            "settle_launches": t["settle_launches"],
             "samples_ms": [round(x, 5) for x in t["samples_ms"]]}
 
 

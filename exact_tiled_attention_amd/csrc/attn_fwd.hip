@@ -98,7 +98,7 @@ __device__ inline float max_pair32(float x) {
 // (padded layout only).  EMU: 0, 2 or 4 of every 8 exponentials of a key chunk by the
 // software exp2 on the FMA pipe (padded layout without dropout only).
 template <typename T, int D, int QB, int RW, int KS, bool VL, bool CAUSAL, bool DROP, int EMU = 0>
-__global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(RW * KS * kWave) __attribute__((amdgpu_waves_per_eu(RW * KS / 4)))
 void fwd_kernel(FwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
@@ -350,8 +350,16 @@ void fwd_kernel(FwdArgs a) {
       const float e0 = fast_exp2(fmaf(sc[kbk][hb + 2 * jj], c, -m_use));
       const float x1 = fmaf(sc[kbk][hb + 2 * jj + 1], c, -m_use);
       const float e1 = (EMU == 4 || (EMU == 2 && (jj & 1))) ? soft_exp2(x1) : fast_exp2(x1);
-      l0 += e0;
-      l1 += e1;
+      if (!DROP && EMU == 0 && cc == 0 && jj == 0) {
+        // the step's first terms start the partial sums (0 + e is not folded by the
+        // compiler, as it would be wrong for e = -0; e >= +0 here).  Not in the dropout
+        // and emulated-exponential forms, where the changed schedule spills registers.
+        l0 = e0;
+        l1 = e1;
+      } else {
+        l0 += e0;
+        l1 += e1;
+      }
       if constexpr (DROP) {
         const u32x4& wv = jj < 2 ? w0 : w1;
         const float k0 = wv[2 * (jj & 1)] >= a.drop.thresh ? e0 : 0.f;
@@ -610,37 +618,57 @@ hipError_t launch_fwd_t(const FwdArgs& a0, hipStream_t stream) {
   const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
   const dim3 block(RW * KS * kWave);
   const bool vl = a.cu_q != nullptr;
-  if (a.causal) {
-    if (vl)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true, false>), grid, block, 0, stream, a);
-    else if (a.dropout)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, true>), grid, block, 0, stream, a);
-    else if (a.exp_emulated == 2)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false, 2>), grid, block, 0, stream, a);
-    else if (a.exp_emulated == 4)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false, 4>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false>), grid, block, 0, stream, a);
+  if constexpr (D == 64 && QB == 1) {
+    // the twelve-wave form is built for the plain forward only (the dropout and emulated
+    // forms need more than its 168 registers): those take the eight-wave 2 x 4 form
+    if (a.dropout || a.exp_emulated) return launch_fwd_t<T, 64, 2, 2, 4>(a0, stream);
+    if (a.causal) {
+      if (vl)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true, false>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false>), grid, block, 0, stream, a);
+    } else {
+      if (vl)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false, false>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
   } else {
-    if (vl)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false, false>), grid, block, 0, stream, a);
-    else if (a.dropout)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, true>), grid, block, 0, stream, a);
-    else if (a.exp_emulated == 2)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false, 2>), grid, block, 0, stream, a);
-    else if (a.exp_emulated == 4)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false, 4>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false>), grid, block, 0, stream, a);
+    if (a.causal) {
+      if (vl)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, true, false>), grid, block, 0, stream, a);
+      else if (a.dropout)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, true>), grid, block, 0, stream, a);
+      else if (a.exp_emulated == 2)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false, 2>), grid, block, 0, stream, a);
+      else if (a.exp_emulated == 4)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false, 4>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, true, false>), grid, block, 0, stream, a);
+    } else {
+      if (vl)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, true, false, false>), grid, block, 0, stream, a);
+      else if (a.dropout)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, true>), grid, block, 0, stream, a);
+      else if (a.exp_emulated == 2)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false, 2>), grid, block, 0, stream, a);
+      else if (a.exp_emulated == 4)
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false, 4>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fwd_kernel<T, D, QB, RW, KS, false, false, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
-// Eight waves per workgroup.  Head dimension 64: two query blocks per wave, 4 row
-// waves x 2 key ranges (256 rows) when that gives every compute unit a workgroup,
-// else 2 row waves x 4 key ranges (128 rows).  Head dimension 128 (register bound):
-// one query block per wave, 8 row waves (256 rows), or 4 x 2 key ranges (128 rows)
-// for grids under two workgroups per compute unit.
+// Head dimension 64: two query blocks per wave, 4 row waves x 2 key ranges (256 rows,
+// eight waves, two per SIMD) when that gives every compute unit a workgroup; else one
+// query block per wave (167 registers) in twelve-wave workgroups of 4 row waves x 3 key
+// ranges (128 rows, three waves per SIMD: more waves to cover each other's stalls).
+// Head dimension 128 (register bound): one query block per wave, 8 row waves (256
+// rows), or 4 x 2 key ranges (128 rows) for grids under two workgroups per compute unit.
+// The waves per SIMD of a launch are its waves / 4 (amdgpu_waves_per_eu above).
 constexpr int kCUs = 256;
 
 template <typename T>
@@ -648,7 +676,7 @@ hipError_t launch_fwd_dtype(const FwdArgs& a, hipStream_t stream) {
   const int64_t wgs256 = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
   if (a.d == 64) {
     if (wgs256 >= kCUs) return launch_fwd_t<T, 64, 2, 4, 2>(a, stream);
-    return launch_fwd_t<T, 64, 2, 2, 4>(a, stream);
+    return launch_fwd_t<T, 64, 1, 4, 3>(a, stream);
   }
   if (wgs256 >= 2 * kCUs) return launch_fwd_t<T, 128, 1, 8, 1>(a, stream);
   return launch_fwd_t<T, 128, 1, 4, 2>(a, stream);
