@@ -203,8 +203,6 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
     return ATTN_ERR_NULL;
   int st = check_dims(B, Hq, Hkv, Sq, Sk, d, false);
   if (st != ATTN_OK) return st;
-  if (d != 128) return ATTN_ERR_HEADDIM;
-  if (causal) return ATTN_ERR_ARG;
   if (o_dtype != ATTN_BF16 && o_dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_ARG;
   Fp8Args a = {};
@@ -213,6 +211,7 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
   a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.group = Hq / Hkv;
+  a.causal = causal != 0;
   a.o_f32 = o_dtype == ATTN_F32;
   a.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(attn_launch_fwd_fp8(a, (hipStream_t)stream));

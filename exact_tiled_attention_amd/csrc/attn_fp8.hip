@@ -35,12 +35,12 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int D = 128;
 constexpr int BC = 64;
 constexpr int SCALE_ROWS = 128;
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
+template <int D>
 struct Fp8Lds {
   static constexpr int KSTR = D + 8;      // bf16 elements per K row (widened from E4M3)
   static constexpr int VSTR = BC + 16;    // bytes per V^T row (E4M3)
@@ -79,9 +79,11 @@ __device__ inline float max_pair32(float x) {
 
 __device__ inline int vt_pos(int k) { return 32 * ((k >> 2) & 1) + ((k >> 3) << 2) + (k & 3); }
 
-template <int NW, bool OF32>
+template <int D, int NW, bool OF32>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void fp8_fwd_kernel(Fp8Args a) {
-  typedef Fp8Lds L;
+  // causal masking is a runtime flag: the plans and the per-lane key limit below carry it
+  const bool CAUSAL = a.causal != 0;
+  typedef Fp8Lds<D> L;
   constexpr int NT = NW * kWave;
   constexpr int BQ = NW * 32;
   constexpr int K_LOADS = (BC * D / 16 + NT - 1) / NT;     // 16-byte K chunks per thread
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   const int BH = a.B * a.Hq;
   const int wg = blockIdx.x;
   const int bh = wg % BH;
-  const int qt = wg / BH;
+  const int qt = CAUSAL ? (a.nqt - 1 - wg / BH) : (wg / BH);   // heavy causal tiles first
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int kvh = h / a.group;
@@ -113,7 +115,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 
   const int q0 = qt * BQ;
   const int qrow = q0 + w * 32 + n;
-  const TilePlan plan = plan_rows(q0, min(q0 + BQ, a.Sq), a.Sq, a.Sk, BC, 0);
+  const TilePlan plan = plan_rows(q0, min(q0 + BQ, a.Sq), a.Sq, a.Sk, BC, CAUSAL);
+  // this wave's rows: the tiles it visits and the first one that needs a mask
+  const int w0 = q0 + w * 32;
+  const TilePlan wplan = plan_rows(w0, max(min(w0 + 32, a.Sq), w0 + 1), a.Sq, a.Sk, BC, CAUSAL);
+  // keys at or past klim are invisible to this lane's query (tail; causal band)
+  const int klim = CAUSAL ? min(a.Sk, qrow + (a.Sk - a.Sq) + 1) : a.Sk;
   const float dq = qrow < a.Sq ? a.q_scale[(int64_t)(b * a.Hq + h) * nqb + qrow / SCALE_ROWS] : 0.f;
   // score factor without the K descale; a negative score scale is moved into Q (sign
   // flip of the bf16 operand) so that the factor is >= 0
@@ -230,14 +237,15 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     // is taken on the raw accumulators (csc >= 0: descales are positive and a negative
     // score scale is moved into Q), so x enters only through one FMA below.
     const float csc = c_q * dk;
+    // visibility of register i of key block kbk: its key offset against this lane's
+    // limit (the per-register offsets are constants, one compare each)
+    const int lim = klim - t * BC - 4 * grp;
+    auto vis = [&](int kbk, int i) { return !MASKED || (kbk * 32 + 8 * (i >> 2) + (i & 3)) < lim; };
     if constexpr (MASKED) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t * BC + kbk * 32 + 8 * (i >> 2) + 4 * grp + (i & 3);
-          s[kbk][i] = key < a.Sk ? s[kbk][i] : -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i) s[kbk][i] = vis(kbk, i) ? s[kbk][i] : -INFINITY;
     }
     float r0 = vmax(s[0][0], s[0][1]), r1 = vmax(s[0][2], s[0][3]);
 #pragma unroll
@@ -258,9 +266,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        // masked cells hold -inf: fma(-inf, csc, .) = -inf -> u = 0 (csc > 0)
-        const float u0 = fast_exp2(fmaf(s[kbk][i], csc, -m_off));
-        const float u1 = fast_exp2(fmaf(s[kbk][i + 1], csc, -m_off));
+        // masked cells give u = 0 by selection (a zero descale or scale makes csc = 0,
+        // and fma(-inf, 0, .) would be NaN)
+        float u0 = fast_exp2(fmaf(s[kbk][i], csc, -m_off));
+        float u1 = fast_exp2(fmaf(s[kbk][i + 1], csc, -m_off));
+        if constexpr (MASKED) {
+          u0 = vis(kbk, i) ? u0 : 0.f;
+          u1 = vis(kbk, i + 1) ? u1 : 0.f;
+        }
         s[kbk][i] = u0;
         s[kbk][i + 1] = u1;
         rs0 += u0;
@@ -271,9 +284,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     m_i = m_new;
     // The accumulator is kept in units of the current V descale s_v: moving to a tile
     // with descale dv (and a moved max) multiplies it by alpha s_v / dv, skipped when
-    // that is 1 in every lane (same scale block, unmoved max).
-    const float beta = alpha * (s_v / dv);
-    s_v = dv;
+    // that is 1 in every lane (same scale block, unmoved max).  A zero V descale (an
+    // all-zero value block) makes the tile's values zero: the accumulator keeps its
+    // frame and the tile adds nothing (dv is the same for every lane of the workgroup).
+    const bool v_zero = !(dv != 0.f);
+    const float beta = v_zero ? alpha : alpha * (s_v / dv);
+    if (!v_zero) s_v = dv;
     if (wave_any(beta != 1.f)) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       const int i0 = 4 * (wd & 3);
       int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[kbk][i0], s[kbk][i0 + 1], 0, false);
       v = __builtin_amdgcn_cvt_pk_fp8_f32(s[kbk][i0 + 2], s[kbk][i0 + 3], v, true);
-      pb[wd] = v;
+      pb[wd] = v_zero ? 0 : v;     // a zero-valued tile adds nothing in the current frame
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -309,10 +325,14 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   for (int t = 0; t < nt; ++t) {
     const int stage = t & 1;
     if (t + 1 < nt) load_tile(t + 1);
-    if (t >= plan.first_masked)
-      compute_tile(std::true_type{}, t, stage);
-    else
-      compute_tile(std::false_type{}, t, stage);
+    // a wave whose rows see nothing of tile t (causal band) skips it; every wave still
+    // stages and passes the barrier
+    if (t < wplan.n_visit) {
+      if (t >= wplan.first_masked)
+        compute_tile(std::true_type{}, t, stage);
+      else
+        compute_tile(std::false_type{}, t, stage);
+    }
     if (t + 1 < nt) store_tile(stage ^ 1);
     __syncthreads();
   }
@@ -343,16 +363,21 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-template <int NW>
+template <int D, int NW>
 hipError_t launch_fp8(const Fp8Args& a0, hipStream_t stream) {
   Fp8Args a = a0;
   a.nqt = (a.Sq + NW * 32 - 1) / (NW * 32);
   const dim3 grid((unsigned)(a.nqt * a.B * a.Hq));
   if (a.o_f32)
-    hipLaunchKernelGGL((fp8_fwd_kernel<NW, true>), grid, dim3(NW * kWave), 0, stream, a);
+    hipLaunchKernelGGL((fp8_fwd_kernel<D, NW, true>), grid, dim3(NW * kWave), 0, stream, a);
   else
-    hipLaunchKernelGGL((fp8_fwd_kernel<NW, false>), grid, dim3(NW * kWave), 0, stream, a);
+    hipLaunchKernelGGL((fp8_fwd_kernel<D, NW, false>), grid, dim3(NW * kWave), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int NW>
+hipError_t launch_fp8_c(const Fp8Args& a, hipStream_t stream) {
+  return launch_fp8<D, NW>(a, stream);
 }
 
 }  // namespace
@@ -364,6 +389,6 @@ int attn_fp8_tile_keys() { return BC; }
 // rows ([4,16,8192,128]: 2.93 -> 2.37 ms); four otherwise.
 hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
   const int64_t wgs256 = (int64_t)((a.Sq + 255) / 256) * a.B * a.Hq;
-  if (wgs256 >= 256) return launch_fp8<8>(a, stream);
-  return launch_fp8<4>(a, stream);
+  if (a.d == 64) return wgs256 >= 256 ? launch_fp8_c<64, 8>(a, stream) : launch_fp8_c<64, 4>(a, stream);
+  return wgs256 >= 256 ? launch_fp8_c<128, 8>(a, stream) : launch_fp8_c<128, 4>(a, stream);
 }

@@ -42,6 +42,7 @@ struct Fp8Args {
   float* lse;
   int B, Hq, Hkv, Sq, Sk, d;
   int group;
+  int causal;
   int o_f32;          // 1: float32 output, 0: bf16 output
   float scale_log2;
   int nqt;

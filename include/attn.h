@@ -184,9 +184,10 @@ int attn_fp8_quantize(const void* x, attn_dtype_t dtype, int B, int H, int S, in
  *       descales, one per 128-row block of the row axis                        (in)
  *   o   [B,Hq,Sq,d]: o_dtype ATTN_BF16 or ATTN_F32                             (out)
  *   lse [B,Hq,Sq] float32 (may be NULL)                                        (out)
- *   Only d = 128 and causal = 0 are supported in this release (ATTN_ERR_HEADDIM /
- *   ATTN_ERR_ARG otherwise).  K/V tiles of attn_fp8_kv_tile() keys are visited in
- *   ascending order, which fixes the frame in which each probability is rounded.
+ *   d = 64 or 128; causal as attn_fwd (bottom-right; masked cells get u = 0).  K/V
+ *   tiles of attn_fp8_kv_tile() keys are visited in ascending order, which fixes the
+ *   frame in which each probability is rounded.  A zero descale (an all-zero block)
+ *   or a zero scale is valid: a zero value descale makes its tile add nothing.
  */
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                  const float* q_scale, const float* k_scale, const float* v_scale,

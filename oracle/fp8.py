@@ -27,6 +27,8 @@ import math
 
 import numpy as np
 
+from . import dense
+
 E4M3_MAX = 448.0
 PROB_OFFSET_LOG2 = 8
 
@@ -90,8 +92,13 @@ def rounding_alternative(u, rel: float):
 
 def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 64,
             scale_rows: int = 128, rows=None, heads=None, prob_round=round_e4m3, frame="running",
-            envelope_rel=None):
-    """The quantised forward, step by step (non-causal).
+            envelope_rel=None, causal: bool = False):
+    """The quantised forward, step by step.
+
+    ``causal``: the bottom-right causal mask (key k visible to row i iff
+    k <= i + S_k - S_q), applied to S before the row max; masked cells give u = 0, a
+    tile with no visible key leaves a row's state unchanged, and a row that sees no key
+    at all gets O = 0 and LSE = -inf (as in the dense definition).
 
     q8/k8/v8: E4M3FN codes [B,H,S,d] (uint8); *_scale: float32 [B,H,ceil(S/128)].
     ``block_c``: K/V tile width; each tile must lie inside one 128-row scale block.
@@ -121,9 +128,10 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
         kv = h // g
         Qi = Q[b, h][rows]
         dq = qs[b, h][rows // scale_rows]
+        vis_all = dense.visible(Sq, Sk, causal, rows=rows)
         if frame == "final":
             S_all = float(scale) * dq[:, None] * (Qi @ K[b, kv].T) * ks[b, kv][np.arange(Sk) // scale_rows][None, :]
-            m_final = S_all.max(axis=1)
+            m_final = np.where(vis_all, S_all, -np.inf).max(axis=1)
         m = np.full(len(rows), -np.inf)
         l = np.zeros(len(rows))
         o = np.zeros((len(rows), V.shape[3]))
@@ -132,14 +140,19 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
             k1 = min(Sk, k0 + block_c)
             dk = ks[b, kv][k0 // scale_rows]
             dv = vs[b, kv][k0 // scale_rows]
+            vis = vis_all[:, k0:k1]
             S = float(scale) * dq[:, None] * dk * (Qi @ K[b, kv][k0:k1].T)
+            S = np.where(vis, S, -np.inf)
             m_new = np.maximum(m, S.max(axis=1))
-            alpha = np.exp(m - m_new)
-            u = off * np.exp(S - m_new[:, None])
+            with np.errstate(invalid="ignore"):
+                # a row that has seen no visible key yet keeps m = -inf and alpha = 1
+                alpha = np.where(m_new == -np.inf, 1.0, np.exp(m - m_new))
+                u = np.where(vis, off * np.exp(S - m_new[:, None]), 0.0)
             if frame == "final":
                 # the same u expressed in the final frame, rounded there, brought back
-                shift = np.exp(m_new - m_final)[:, None]
-                p8 = prob_round(u * shift) / shift
+                with np.errstate(invalid="ignore", over="ignore"):
+                    shift = np.where(m_new == -np.inf, 1.0, np.exp(m_new - m_final))[:, None]
+                p8 = np.where(u > 0, prob_round(u * shift) / shift, 0.0)
             else:
                 p8 = prob_round(u)
             l = alpha * l + u.sum(axis=1)
@@ -148,10 +161,12 @@ def forward(q8, k8, v8, q_scale, k_scale, v_scale, scale: float, block_c: int = 
                 flip = np.abs(rounding_alternative(u, envelope_rel) - p8)
                 e = alpha[:, None] * e + dv * (flip @ np.abs(V[b, kv][k0:k1]))
             m = m_new
-        O[b, h] = o / l[:, None]
-        LSE[b, h] = m + np.log(l) - PROB_OFFSET_LOG2 * math.log(2.0)
-        if E is not None:
-            E[b, h] = e / l[:, None]
+        empty = ~(l > 0)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            O[b, h] = np.where(empty[:, None], 0.0, o / l[:, None])
+            LSE[b, h] = np.where(empty, -np.inf, m + np.log(l) - PROB_OFFSET_LOG2 * math.log(2.0))
+            if E is not None:
+                E[b, h] = np.where(empty[:, None], 0.0, e / l[:, None])
     if E is not None:
         return O, LSE, E
     return O, LSE

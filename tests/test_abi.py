@@ -123,7 +123,7 @@ def test_decode_and_fp8_checks():
         a.update(kw)
         return lib.attn_fwd_fp8(P, P, P, P, P, P, P, None, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], d,
                                 0.088, causal, odt, None)
-    assert f8(d=64) == -4 and f8(causal=1) == -8 and f8(odt=0) == -5 and f8(Sk=0) == -2
+    assert f8(d=32) == -4 and f8(odt=0) == -5 and f8(Sk=0) == -2 and f8(Hkv=3) == -3
 
 
 def test_decode_pick_chunk():

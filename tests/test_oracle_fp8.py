@@ -44,19 +44,25 @@ def _small_inputs(seed=7, B=1, H=2, S=200, d=32):
 
 
 @pytest.mark.parametrize("block_c", [32, 64, 128])
-def test_without_probability_rounding_steps_reduce_to_dense(block_c):
+@pytest.mark.parametrize("causal,Sq,Sk", [(False, 200, 200), (True, 200, 200), (True, 150, 260), (True, 260, 150)])
+def test_without_probability_rounding_steps_reduce_to_dense(block_c, causal, Sq, Sk):
     """Removing the P rounding, the 2^8 offset, the scale placement and the LSE shift
-    must reproduce the dense definition on the dequantised inputs exactly (fp64)."""
-    w = _small_inputs()
+    must reproduce the dense definition on the dequantised inputs exactly (fp64),
+    causal masks included (S_q > S_k: rows that see no key get O = 0, LSE = -inf)."""
+    w = attn_inputs.fp8_prefill(1, 2, 2, Sq, Sk, 32, seed=7)
     t, p = w.tensors, w.params
     O, L = fp8.forward(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"], p["scale"],
-                       block_c=block_c, prob_round=lambda u: u)
+                       block_c=block_c, prob_round=lambda u: u, causal=causal)
     Qd = fp8.dequantized(t["q8"], t["q_scale"])
     Kd = fp8.dequantized(t["k8"], t["k_scale"])
     Vd = fp8.dequantized(t["v8"], t["v_scale"])
-    Od, Ld = dense.forward(Qd, Kd, Vd, p["scale"], False)
+    Od, Ld = dense.forward(Qd, Kd, Vd, p["scale"], causal)
     assert np.allclose(O, Od, atol=1e-11, rtol=1e-11)
-    assert np.allclose(L, Ld, atol=1e-11)
+    assert np.array_equal(np.isneginf(L), np.isneginf(Ld))
+    fin = np.isfinite(Ld)
+    assert np.allclose(L[fin], Ld[fin], atol=1e-11)
+    if causal and Sq > Sk:
+        assert np.isneginf(L).any() and np.all(O[np.isneginf(L)] == 0)
 
 
 # ---------------------------------------------------------------------------------
@@ -203,3 +209,15 @@ def test_envelope_is_zero_without_ambiguity_and_bounds_a_flip():
     Of, _ = fp8.forward(*args, block_c=64, prob_round=lambda u: fp8.rounding_alternative(u, 0.05))
     assert np.all(np.abs(Of - O1) <= E1 + 1e-12)
     assert E1.max() > 0
+
+
+def test_pin_causal_row_sees_only_its_keys():
+    """Causal, S_q = S_k = 2 (one tile): row 0 sees key 0 only, so its O is V_0 (the
+    value 1.0 exactly: u = 256, p8 = 256) and LSE = S_00 = 0; row 1 sees both keys,
+    scores (0, -1): u = (256, 94.18) -> p8 = (256, 96)."""
+    q = _codes([C_ONE, C_ONE])
+    O, L = fp8.forward(q, _codes([C_ZERO, C_MINUS_ONE]), _codes([C_ONE, C_TWO]), _descales([1.0]),
+                       _descales([1.0]), _descales([1.0]), 1.0, block_c=2, causal=True)
+    assert O[0, 0, 0, 0] == 1.0 and L[0, 0, 0] == 0.0
+    l = 256.0 * (1.0 + math.exp(-1.0))
+    assert abs(O[0, 0, 1, 0] - (256.0 * 1.0 + 96.0 * 2.0) / l) < 1e-13
