@@ -13,7 +13,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, LibraryMissing, lib
 
-__all__ = ["attn_fwd", "attn_fwd_exp_emulated", "exp2_soft", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
+__all__ = ["attn_fwd", "attn_fwd_exp_emulated", "exp2_soft", "attn_fwd_varlen", "attn_decode_paged", "attn_fwd_dropout", "fp8_quantize", "attn_fwd_fp8", "attn_bwd_fp8", "attn_bwd", "attn_decode_splitkv", "attn_decode_splitkv_noalloc",
            "bwd_workspace_size", "decode_workspace_size", "fp8_kv_tile",
            "AttnError", "LibraryMissing", "lib"]
 
@@ -209,6 +209,50 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, scale=None, o_dtype=torc
                             _stream(stream))
     _lib.check("attn_fwd_fp8", st)
     return o, lse
+
+
+def attn_bwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, do, scale=None, causal=False,
+                 grad_dtype=torch.float32, workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """dQ, dK, dV with respect to the dequantised operands of attention on E4M3 codes
+    (as attn_fwd_fp8 takes them); o and do bf16, lse float32."""
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        if t.dtype not in _FP8_CODE_DTYPES:
+            raise TypeError(f"{n} must hold E4M3FN codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale"), (lse, "lse")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{n} must be float32, got {t.dtype}")
+    for t, n in ((o, "o"), (do, "do")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16, got {t.dtype}")
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8"), (o, "o"), (do, "do")):
+        _require(t, n, 4)
+    B, Hq, Sq, d = q8.shape
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    dev = q8.device
+    _expect(k8, "k8", (B, Hkv, Sk, d), k8.dtype, dev)
+    _expect(v8, "v8", (B, Hkv, Sk, d), v8.dtype, dev)
+    _expect(q_scale, "q_scale", (B, Hq, (Sq + 127) // 128), torch.float32, dev)
+    _expect(k_scale, "k_scale", (B, Hkv, (Sk + 127) // 128), torch.float32, dev)
+    _expect(v_scale, "v_scale", (B, Hkv, (Sk + 127) // 128), torch.float32, dev)
+    _expect(o, "o", (B, Hq, Sq, d), torch.bfloat16, dev)
+    _expect(do, "do", (B, Hq, Sq, d), torch.bfloat16, dev)
+    _expect(lse, "lse", (B, Hq, Sq), torch.float32, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty((B, Hq, Sq, d), dtype=grad_dtype, device=dev) if dq is None else dq
+    dk = torch.empty((B, Hkv, Sk, d), dtype=grad_dtype, device=dev) if dk is None else dk
+    dv = torch.empty((B, Hkv, Sk, d), dtype=grad_dtype, device=dev) if dv is None else dv
+    _expect(dq, "dq", (B, Hq, Sq, d), grad_dtype, dev)
+    _expect(dk, "dk", (B, Hkv, Sk, d), grad_dtype, dev)
+    _expect(dv, "dv", (B, Hkv, Sk, d), grad_dtype, dev)
+    need = bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib().attn_bwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(o),
+                            _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale,
+                            int(bool(causal)), _code(grad_dtype), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("attn_bwd_fp8", st)
+    return dq, dk, dv
 
 
 def bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d) -> int:

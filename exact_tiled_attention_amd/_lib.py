@@ -36,6 +36,8 @@ PROTOTYPES = {
     "attn_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _I, _P]),
     "attn_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32,
                               _I, _I, _I, _I, _P, _S, _P]),
+    "attn_bwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P, _S,
+                          _P]),
     "attn_bwd_deterministic_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_bwd_deterministic": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I,
                                     _P, _S, _P]),

@@ -256,6 +256,39 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
 }
 
+int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
+                 const float* v_scale, const void* o, const float* lse, const void* dO, void* dq, void* dk,
+                 void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 attn_dtype_t grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q8 == nullptr || k8 == nullptr || v8 == nullptr || q_scale == nullptr || k_scale == nullptr ||
+      v_scale == nullptr || o == nullptr || lse == nullptr || dO == nullptr || dq == nullptr ||
+      dk == nullptr || dv == nullptr)
+    return ATTN_ERR_NULL;
+  int st = check_dims(B, Hq, Hkv, Sq, Sk, d, false);
+  if (st != ATTN_OK) return st;
+  if (grad_dtype != ATTN_F32 && grad_dtype != ATTN_BF16 && grad_dtype != ATTN_F16) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_ARG;
+  if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;   // one grid row per (b, kv head)
+  const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  const size_t rows = (size_t)B * Hq * Sq;
+  BwdArgs a = {};
+  a.q = q8; a.k = k8; a.v = v8; a.o = o; a.lse = lse; a.dO = dO;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = (float*)workspace;
+  a.delta = (float*)((char*)workspace + align256(rows * d * sizeof(float)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
+  a.group = Hq / Hkv;
+  a.causal = causal != 0;
+  a.dtype_bf16 = 1;            // o and dO are bf16
+  a.grad_type = (int)grad_dtype;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.fp8 = 1;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+}
+
 size_t attn_bwd_deterministic_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                              int dq_splits) {
   if (check_dims(B, Hq, Hkv, Sq, Sk, d, false) != ATTN_OK) return 0;

@@ -170,11 +170,28 @@ __device__ inline void split_pack4x2(const f32x4& x0, const f32x4& x1, u32x4& hi
   }
 }
 
+// 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
+__device__ inline u32x4 e4m3x8_bf16(const u32x2& w) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  return u32x4{Elem<bf16>::pack2(a[0], a[1]), Elem<bf16>::pack2(b[0], b[1]), Elem<bf16>::pack2(c[0], c[1]),
+               Elem<bf16>::pack2(d[0], d[1])};
+}
+
 // DQ: also add dS K into the float32 dQ accumulator (atomics); without it the kernel
 // produces dK and dV only (deterministic mode computes dQ in bwd_dq_kernel).
 // DROP: regenerate the forward's dropout decisions Z (keep / (1 - p)) and use
 // dV += (P Z)^T dO, dS = P (Z dP - D).
-template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool DROP>
+// F8 (T = bf16): Q, K, V are E4M3 codes with per-128-row float32 descales, widened
+// exactly to bf16 in LDS; the gradients are those of attention on the dequantised
+// operands Q_d = dQ Q8, K_d = dK K8, V_d = dV V8.  A 128-key tile is one descale block
+// and a 32-query step lies in one, so the descales are per-step and per-workgroup
+// scalars: S = (scale dQ dK) Q8 K8^T, dP = dV (dO V8^T), dK_d = scale sum (dQ dS)^T Q8,
+// dQ_d = scale dK sum dS K8, dV_d = P^T dO.
+template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool DROP, bool F8 = false>
 __global__ __launch_bounds__(kNTM) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_main_kernel(BwdArgs a) {
   typedef M16<T> MF;
@@ -216,10 +233,18 @@ void bwd_main_kernel(BwdArgs a) {
   const bool key_tail = (k0 + kBKV) > a.Sk;
   const int delta = a.Sk - a.Sq;
 
-  const T* kbase = reinterpret_cast<const T*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)a.Sk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)a.Sk * D * 2);
+  constexpr int EB = F8 ? 1 : 2;            // bytes per stored Q / K / V element
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * EB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * EB;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)a.Sk * D * EB);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)a.Sk * D * EB);
+  // fp8: this workgroup's key and value descales (its 128 keys are one scale block)
+  float dk_s = 1.f, dv_s = 1.f;
+  if constexpr (F8) {
+    const int nkb = (a.Sk + kBKV - 1) / kBKV;
+    dk_s = a.k_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
+    dv_s = a.v_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
+  }
 
   // The K and V tiles, row-major, in LDS (keys past S_k read as zero): the B operands
   // of S and dP (column = key, slots d 32kc + 8g ..) and the K operand of dQ.
@@ -229,10 +254,15 @@ void bwd_main_kernel(BwdArgs a) {
     for (int r = 0; r < KCH; ++r) {
       const int idx = r * kNTM + tid;
       const int row = idx / CPR;
-      const uint32_t src = (uint32_t)((k0 + row) * D + 8 * (idx % CPR)) * 2;
+      const uint32_t src = (uint32_t)((k0 + row) * D + 8 * (idx % CPR)) * EB;
       const int dst = row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16);
-      st_lds_16(lds + L::K + dst, buf_load_16(krs, src));
-      st_lds_16(lds + L::V + dst, buf_load_16(vrs, src));
+      if constexpr (F8) {
+        st_lds_16(lds + L::K + dst, e4m3x8_bf16(buf_load_8(krs, src)));
+        st_lds_16(lds + L::V + dst, e4m3x8_bf16(buf_load_8(vrs, src)));
+      } else {
+        st_lds_16(lds + L::K + dst, buf_load_16(krs, src));
+        st_lds_16(lds + L::V + dst, buf_load_16(vrs, src));
+      }
     }
   }
 
@@ -253,6 +283,7 @@ void bwd_main_kernel(BwdArgs a) {
   const int st_t = tid % (kNTM / 2);
   u32x4 sreg[SCH];
   float slse = 0.f, sdel = 0.f;
+  const int nqb = (a.Sq + kBKV - 1) / kBKV;   // fp8: query descale blocks per head
 
   auto step_coords = [&](int step, int& h, int& qt) {
     h = kvh * a.group + step / nq;
@@ -261,12 +292,20 @@ void bwd_main_kernel(BwdArgs a) {
   auto prefetch = [&](int step) {
     int h, qt;
     step_coords(step, h, qt);
-    const T* src = reinterpret_cast<const T*>(stage_do ? a.dO : a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * 2);
+    // fp8: Q holds one-byte codes (widened when staged), dO 16-bit values
+    const int eb = (F8 && !stage_do) ? 1 : 2;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(stage_do ? a.dO : a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D * eb;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * eb);
 #pragma unroll
     for (int r = 0; r < SCH; ++r) {
       const int idx = r * (kNTM / 2) + st_t;
-      sreg[r] = buf_load_16(rs, (uint32_t)((qt * BQ + idx / CPR) * D + 8 * (idx % CPR)) * 2);
+      const uint32_t off = (uint32_t)((qt * BQ + idx / CPR) * D + 8 * (idx % CPR));
+      if (F8 && !stage_do) {
+        const u32x2 c8 = buf_load_8(rs, off);
+        sreg[r] = u32x4{c8.x, c8.y, 0u, 0u};
+      } else {
+        sreg[r] = buf_load_16(rs, off * 2);
+      }
     }
     if (tid < BQ) {
       const int qr = qt * BQ + tid;
@@ -281,7 +320,8 @@ void bwd_main_kernel(BwdArgs a) {
     for (int r = 0; r < SCH; ++r) {
       const int idx = r * (kNTM / 2) + st_t;
       const int row = idx / CPR;
-      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), sreg[r]);
+      const u32x4 val = (F8 && !stage_do) ? e4m3x8_bf16(u32x2{sreg[r].x, sreg[r].y}) : sreg[r];
+      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), val);
     }
     if (tid < BQ) {
       s_lse[sb][tid] = slse;
@@ -307,6 +347,13 @@ void bwd_main_kernel(BwdArgs a) {
   // MASKED applies the element mask (tails and the causal band).
   auto compute = [&](auto masked_tag, int qt, int h, int sb) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    // fp8: the step's query descale (its 32 rows lie in one 128-row block); the score
+    // factor takes dQ dK, the dK product takes dQ through dS
+    float dq_s = 1.f, sl2 = a.scale_log2;
+    if constexpr (F8) {
+      dq_s = a.q_scale[(int64_t)(b * a.Hq + h) * nqb + (qt * BQ) / kBKV];
+      sl2 = a.scale_log2 * dq_s * dk_s;
+    }
     // Dropout decisions, first (their temporaries never meet the products' registers),
     // as bit 4t + i for query 16t + 4g + i.  The lane's key is mykey; the four lanes of a
     // key quad (n = 4a .. 4a+3) share the Philox counter word mykey / 4, so each computes
@@ -361,7 +408,7 @@ void bwd_main_kernel(BwdArgs a) {
       const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[sb][qb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float pv = fast_exp2(fmaf(s[t][i], a.scale_log2, -lv[i]));
+        float pv = fast_exp2(fmaf(s[t][i], sl2, -lv[i]));
         if constexpr (MASKED) {
           const int qr = qt * BQ + qb + i;
           const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
@@ -372,7 +419,7 @@ void bwd_main_kernel(BwdArgs a) {
           z = ((keepbits >> (4 * t + i)) & 1u) ? a.drop.rp : 0.f;
         }
         s[t][i] = pv * z;
-        dp[t][i] = pv * (z * dp[t][i] - dl[i]);
+        dp[t][i] = pv * (z * (F8 ? dv_s * dp[t][i] : dp[t][i]) - dl[i]);
       }
     }
     // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries 4g + i and
@@ -381,7 +428,10 @@ void bwd_main_kernel(BwdArgs a) {
     // bits), so these two sums keep float32-like precision.
     u32x4 pp, pl, ss, sl;
     split_pack4x2<T>(s[0], s[1], pp, pl);
-    split_pack4x2<T>(dp[0], dp[1], ss, sl);
+    if constexpr (F8)
+      split_pack4x2<T>(dp[0] * dq_s, dp[1] * dq_s, ss, sl);
+    else
+      split_pack4x2<T>(dp[0], dp[1], ss, sl);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x2 olo = tr_tile(sdo, 4 * g, 16 * db), ohi = tr_tile(sdo, 16 + 4 * g, 16 * db);
@@ -470,7 +520,7 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int qr = qt * BQ + 16 * tq + 4 * g + i;
-          if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, acc[i]);
+          if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, F8 ? acc[i] * dk_s : acc[i]);
         }
       }
     }
@@ -751,6 +801,19 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.Sk + kBKV - 1) / kBKV), (unsigned)(a.B * a.Hkv));
   const int64_t n4 = rows * D / 4;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (a.fp8) {
+      // E4M3 operands: the atomic-dQ column owner only
+      if (a.causal)
+        hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, true, false, true>), grid, dim3(kNTM), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, true, false, true>), grid, dim3(kNTM), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((bwd_convert_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
+      return hipGetLastError();
+    }
+  }
   if (a.deterministic) {
     if (a.dropout)
       main_k<T, G, D, false, true>(a, grid, stream);

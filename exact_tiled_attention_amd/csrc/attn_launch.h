@@ -75,6 +75,12 @@ struct BwdArgs {
   float* dq_part;
   int dropout;        // 1: regenerate the forward's dropout decisions from `drop`
   DropParams drop;
+  // fp8 operands: q, k, v are E4M3 codes with float32 descales [B, H, ceil(S/128)];
+  // o and dO are bf16 (dtype_bf16 = 1)
+  int fp8;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct DecodeArgs {

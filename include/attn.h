@@ -223,6 +223,34 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_fp8 -- backward of attention on E4M3 operands with per-block descales: the
+ * gradients with respect to the dequantised operands Q_d = dQ Q8, K_d = dK K8,
+ * V_d = dV V8 (one float32 descale per 128-row block, as attn_fwd_fp8 takes them) of
+ * O = softmax(scale Q_d K_d^T + mask) V_d, by the FA2 split of attn_bwd ("M4.4 -
+ * FlashAttention-2 ...", section 0x06.1, Algorithm 2): P = exp(scale Q_d K_d^T - LSE)
+ * recomputed from the caller's LSE, D = rowsum(dO * O) from the caller's O, dV = P^T dO,
+ * dP = dO V_d^T, dS = P (dP - D), dQ = scale dS K_d, dK = scale dS^T Q_d.  The pages
+ * leave FP8 training to future work ("M4.6 - FlashAttention-3/4 Hardware Pipelines",
+ * section 0x06, after its accuracy table), so no quantisation enters the backward: the
+ * E4M3 values are widened exactly to bf16 for the matrix products (float32
+ * accumulation), the descales enter per tile in float32, and the probabilities and dS
+ * enter dV, dK and dQ as hi + lo bf16 pairs as in attn_bwd.  With O and LSE of the exact
+ * forward on the dequantised operands these are the exact gradients; with the outputs of
+ * attn_fwd_fp8 (whose probabilities are rounded to E4M3) its quantisation error reaches
+ * the gradients through D.
+ *
+ *   q8 [B,Hq,Sq,d], k8/v8 [B,Hkv,Sk,d]: E4M3FN bytes; *_scale as attn_fwd_fp8      (in)
+ *   o, dO [B,Hq,Sq,d] bf16; lse [B,Hq,Sq] float32 (natural log)                   (in)
+ *   dq [B,Hq,Sq,d], dk/dv [B,Hkv,Sk,d]: grad_dtype (ATTN_F32, ATTN_BF16, ATTN_F16) (out)
+ *   workspace: >= attn_bwd_workspace_size(...) bytes (float32 dQ accumulator + D)
+ *   d = 64 or 128; causal as attn_fwd; dQ is accumulated with atomics as in attn_bwd.
+ */
+int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
+                 const float* v_scale, const void* o, const float* lse, const void* dO, void* dq, void* dk,
+                 void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 attn_dtype_t grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_bwd_deterministic -- attn_bwd with bitwise-repeatable results (no atomics).
  * "M4.4 - FlashAttention-2 ...", section 0x06.1F (atomic dQ accumulation has no fixed
  * order; the alternative materialises one partial per producer and reduces the

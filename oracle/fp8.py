@@ -227,3 +227,52 @@ def quantize(x, block_rows: int = 128, per_tensor: bool = False):
     u = Xb / desc.astype(np.float64)[..., None, None]
     codes = encode_rne_sat(u).reshape(B, H, nb * block_rows, d)[:, :, :S]
     return codes, desc
+
+
+# ---------------------------------------------------------------------------------
+# Backward on E4M3 operands.  The pages define no FP8 backward ([HW] section 0x06 leaves
+# FP8 training to future work), so this follows the plainest reading: the gradients of
+# attention on the dequantised operands, by the FA2 backward formulas ([FA2] section
+# 0x06.1): P recomputed from the given LSE, D = rowsum(dO * O) from the given O.
+
+def backward(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, do, scale: float, causal: bool = False,
+             heads=None, scale_rows: int = 128):
+    """dQ [B,Hq,Sq,d], dK, dV [B,Hkv,Sk,d] (float64; dK/dV summed over each K/V head's
+    query group) with respect to Q_d = decode(q8) dQ, K_d, V_d:
+
+        S  = scale Q_d K_d^T (masked cells excluded),  P = exp(S - LSE)
+        dV = P^T dO,  dP = dO V_d^T,  D = rowsum(dO * O),  dS = P * (dP - D)
+        dQ = scale dS K_d,  dK = scale dS^T Q_d.
+
+    ``o``, ``lse``: the forward's output and log-sum-exp as the backward receives them.
+    ``heads``: optional (b, h_kv) pairs to evaluate (the rest is NaN)."""
+    Qd = dequantized(q8, q_scale, scale_rows)
+    Kd = dequantized(k8, k_scale, scale_rows)
+    Vd = dequantized(v8, v_scale, scale_rows)
+    O = np.asarray(o.detach().cpu().double().numpy() if hasattr(o, "detach") else o, dtype=np.float64)
+    dO = np.asarray(do.detach().cpu().double().numpy() if hasattr(do, "detach") else do, dtype=np.float64)
+    L = np.asarray(lse.detach().cpu().double().numpy() if hasattr(lse, "detach") else lse, dtype=np.float64)
+    B, Hq, Sq, _ = Qd.shape
+    Hkv, Sk = Kd.shape[1], Kd.shape[2]
+    g = Hq // Hkv
+    vis = dense.visible(Sq, Sk, causal)
+    s = float(scale)
+    dQ = np.full_like(Qd, np.nan)
+    dK = np.full_like(Kd, np.nan)
+    dV = np.full_like(Vd, np.nan)
+    pairs = [(b, kv) for b in range(B) for kv in range(Hkv)] if heads is None else heads
+    for b, kv in pairs:
+        dK[b, kv] = 0.0
+        dV[b, kv] = 0.0
+        for h in range(kv * g, (kv + 1) * g):
+            S = s * (Qd[b, h] @ Kd[b, kv].T)
+            with np.errstate(invalid="ignore", over="ignore"):
+                P = np.where(vis, np.exp(S - L[b, h][:, None]), 0.0)
+            P = np.where(np.isneginf(L[b, h])[:, None], 0.0, P)     # rows with no visible key
+            dV[b, kv] += P.T @ dO[b, h]
+            dP = dO[b, h] @ Vd[b, kv].T
+            D = (dO[b, h] * O[b, h]).sum(axis=1)
+            dS = P * (dP - D[:, None])
+            dQ[b, h] = s * (dS @ Kd[b, kv])
+            dK[b, kv] += s * (dS.T @ Qd[b, h])
+    return dQ, dK, dV

@@ -258,3 +258,17 @@ def test_decode_noalloc_checks_run_before_any_hip_call():
     assert lib.attn_decode_workspace_size(64, 32, 32768, 128, 256) > (64 << 20)
     assert call(B=64, Hq=32, Hkv=8, Smax=32768, chunk=256) == -6
     assert lib.attn_decode_splitkv_noalloc(None, P, P, P, P, None, 2, 8, 2, 512, 128, 0.088, 256, 1, None) == -1
+
+
+def test_bwd_fp8_argument_checks():
+    lib, _ = _lib()
+    ws = lib.attn_bwd_workspace_size(1, 4, 2, 64, 64, 128)
+    def call(d=128, grad=2, ws_bytes=ws, **kw):
+        a = dict(B=1, Hq=4, Hkv=2, Sq=64, Sk=64)
+        a.update(kw)
+        return lib.attn_bwd_fp8(P, P, P, P, P, P, P, P, P, P, P, P, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], d,
+                                0.088, 1, grad, P, ws_bytes, None)
+    assert call(d=96) == -4 and call(grad=3) == -5 and call(Hkv=3) == -3 and call(Sk=0) == -2
+    assert call(ws_bytes=ws - 1) == -6
+    assert lib.attn_bwd_fp8(None, P, P, P, P, P, P, P, P, P, P, P, 1, 4, 2, 64, 64, 128, 0.088, 1, 2, P, ws,
+                            None) == -1

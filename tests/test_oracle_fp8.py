@@ -221,3 +221,39 @@ def test_pin_causal_row_sees_only_its_keys():
     assert O[0, 0, 0, 0] == 1.0 and L[0, 0, 0] == 0.0
     l = 256.0 * (1.0 + math.exp(-1.0))
     assert abs(O[0, 0, 1, 0] - (256.0 * 1.0 + 96.0 * 2.0) / l) < 1e-13
+
+
+@pytest.mark.parametrize("causal,Sq,Sk", [(False, 96, 80), (True, 96, 96), (True, 120, 70)])
+def test_backward_with_exact_o_and_lse_is_the_dense_gradient(causal, Sq, Sk):
+    """Given the exact forward's O and LSE on the dequantised operands, the fp8 backward
+    is the (pinned) exact gradient of the dense definition on those operands."""
+    w = attn_inputs.fp8_prefill(1, 4, 2, Sq, Sk, 16, seed=21)
+    t, p = w.tensors, w.params
+    Qd = fp8.dequantized(t["q8"], t["q_scale"])
+    Kd = fp8.dequantized(t["k8"], t["k_scale"])
+    Vd = fp8.dequantized(t["v8"], t["v_scale"])
+    dO = np.random.default_rng(3).standard_normal(Qd.shape)
+    O, L = dense.forward(Qd, Kd, Vd, p["scale"], causal)
+    got = fp8.backward(t["q8"], t["k8"], t["v8"], t["q_scale"], t["k_scale"], t["v_scale"], O, L, dO,
+                       p["scale"], causal)
+    want = dense.backward(Qd, Kd, Vd, dO, p["scale"], causal)[:3]
+    for g_, w_ in zip(got, want):
+        assert np.allclose(g_, w_, atol=1e-9, rtol=1e-9)
+
+
+def test_backward_descales_matter():
+    """Planted mistakes: ignoring the key descale in S, or the value descale in dP,
+    changes the gradients."""
+    w = attn_inputs.fp8_prefill(1, 2, 2, 64, 200, 16, seed=22)
+    t, p = w.tensors, w.params
+    Qd = fp8.dequantized(t["q8"], t["q_scale"])
+    Kd = fp8.dequantized(t["k8"], t["k_scale"])
+    Vd = fp8.dequantized(t["v8"], t["v_scale"])
+    dO = np.random.default_rng(4).standard_normal(Qd.shape)
+    O, L = dense.forward(Qd, Kd, Vd, p["scale"], False)
+    args = (t["q8"], t["k8"], t["v8"], t["q_scale"])
+    right = fp8.backward(*args, t["k_scale"], t["v_scale"], O, L, dO, p["scale"])
+    for ks, vs in ((torch.ones_like(t["k_scale"]), t["v_scale"]), (t["k_scale"], torch.ones_like(t["v_scale"]))):
+        with np.errstate(all="ignore"):
+            wrong = fp8.backward(*args, ks, vs, O, L, dO, p["scale"])
+        assert any(not np.allclose(a, b, atol=1e-2) for a, b in zip(right, wrong))
