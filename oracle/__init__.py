@@ -16,10 +16,11 @@ Modules:
   dense   -- the dense definition (forward, LSE, backward, decode), its
              packed variable-length form and the paged-cache decode       [pinned]
   state   -- the online (m, l, u, n) state algebra and its merges     [pinned]
-  fp8     -- the E4M3FN codebook and the quantised forward steps      [codebook,
-             the 2^8 cancellation and the no-rounding reduction are pinned;
-             parity of the quantised output itself is unpinned: no printed values
-             exist for this input distribution]
+  fp8     -- the E4M3FN codebook, the quantised forward steps and the
+             backward on E4M3 operands                               [pinned: the
+             codebook, hand-derived cases of each rounding step, the reduction to
+             the dense definition without the rounding, the backward's reduction to
+             the dense exact gradient]
   tiles   -- causal tile classes, visit counts, packed-launch census  [pinned]
   dropout -- Philox4x32-10 keep decisions by element coordinates, the dropout
              forward and its backward                              [pinned]
