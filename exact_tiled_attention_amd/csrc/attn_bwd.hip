@@ -544,6 +544,353 @@ void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------
+// 2b. Column owner with split roles (the plain backward: no dropout, 16-bit operands).
+// One workgroup owns a 128-key tile; four key groups of 32 keys, each served by two
+// waves on one SIMD: wave w (role P) keeps the group's K rows in registers, computes
+// S = Q K^T and P = exp(S - LSE) and accumulates dV += P^T dO; wave w + 4 (role dS)
+// keeps the V rows, computes dP = dO V^T, takes P from its partner through LDS, forms
+// dS = P (dP - D) and accumulates dK += dS^T Q.  Both products of a role use 32x32x16
+// matrix-core tiles with the step's 32 queries and the group's 32 keys, whose
+// accumulator layout (lane = key, registers = queries) is already the A-operand layout
+// of the dV / dK products, and one wave holds one accumulator set (64 registers at
+// d = 128), so two waves share each SIMD and cover each other's waits.  Per step the
+// waves read only the staged Q and dO tiles (fragment and transpose reads).  With DQ,
+// dS goes to LDS key-major and the eight waves compute dQ = dS K in 16x16 tiles over
+// the tile's 128 keys (transpose reads of dS and of the K tile kept in LDS), added
+// with float32 atomics ([FA2] section 0x06.1F).  Q and dO tiles go straight from
+// HBM/L2 into LDS (two slots, one step ahead).  dS has two slots, so the dQ tiles of
+// step t run at the start of step t + 1, after its first barrier: two barriers per step
+// (staged tiles and the previous dS visible; P visible), and the atomics are issued a
+// whole step before the wait that precedes the next barrier.
+constexpr int kKW = 32;               // keys per group
+constexpr int kKG = 4;                // key groups per workgroup
+constexpr int kKVT = kKW * kKG;       // keys per workgroup
+constexpr int kKVW = 2 * kKG;         // waves per workgroup
+constexpr int kKVQ = 32;              // queries per step
+
+template <int D>
+struct KvLds {
+  static constexpr int ROWB = D * 2;
+  static constexpr int QT = kKVQ * ROWB;            // one staged Q or dO tile
+  static constexpr int Q0 = 0;                      // Q slots 0, 1
+  static constexpr int DO0 = 2 * QT;                // dO slots 0, 1
+  static constexpr int K = 4 * QT;                  // K tile [128 keys][D]
+  static constexpr int DS = K + kKVT * ROWB;        // dS slots 0, 1: [128 keys][32 queries], 64-byte rows
+  static constexpr int DSS = 2 * kKVT * kKVQ * 2;   // one slot: the values, then their bf16 residuals
+  static constexpr int P = DS + 2 * DSS;            // P handoff [group][16 registers][64 lanes] float32
+  static constexpr int BYTES = P + kKG * 16 * kWave * 4;
+};
+
+// Chunk swizzle of staged rows (Q, dO, K): chunk p of row r at position p ^ kv_swz(r).
+// The fragment reads take one chunk of 16 consecutive rows (bank groups = low three
+// bits of the position: 2(r&3) + bit 2 of r runs through all eight over 8 rows); the
+// transpose reads take two adjacent chunks of 4 consecutive rows (XOR with 2j + const
+// for j = 0..3 keeps the 8 positions distinct).
+template <int D> __device__ inline int kv_swz(int r) {
+  const int s = 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1);
+  return D == 128 ? s : (s & 7);
+}
+// dS rows: 16-byte unit u of key row r at u ^ 2((r >> 1) & 1) (a transpose read's 4 rows
+// x 2 units then cover the eight bank groups); the residuals follow the values.
+__device__ inline int kv_ds_off(int key, int q) {
+  const int u = q >> 3;
+  return key * (kKVQ * 2) + ((u ^ (2 * ((key >> 1) & 1))) * 16) + (q & 7) * 2;
+}
+
+template <typename T, typename G, int D, bool CAUSAL, bool DQ>
+__global__ __launch_bounds__(kKVW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_kv_kernel(BwdArgs a) {
+  typedef Elem<T> E;
+  typedef typename E::v8 V8;
+  typedef M16<T> MF;
+  typedef KvLds<D> L;
+  constexpr int KC = D / 16;                 // contraction chunks of S and dP
+  constexpr int DB = D / 32;                 // 32-wide d blocks of dK, dV
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int WL = kKVQ * CPR / kWave;     // wave loads (1 KiB each) per staged tile
+  constexpr int DQB = 2 * (D / 16);          // dQ tiles (16 queries x 16 d) per step
+  static_assert(WL * kWave == kKVQ * CPR && kWave % CPR == 0, "staging splits evenly");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
+  __shared__ __attribute__((aligned(16))) float s_lse[2][kKVQ];
+  __shared__ __attribute__((aligned(16))) float s_del[2][kKVQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int grp = w % kKG;                   // key group
+  const bool role_p = w < kKG;               // P / dV wave, else dP / dS / dK wave
+  const int n = lane & 31;
+  const int g = lane >> 5;
+  const int s16 = lane & 15;
+  const int gh = (lane >> 4) & 1;            // which 16-column half a transpose read takes
+
+  // key tiles slowest in the linear order: under causal masking the tiles with the most
+  // visible query tiles start first
+  const int nbkv = a.B * a.Hkv;
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int jt = lin / nbkv;
+  const int bkv = lin - jt * nbkv;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int k0 = jt * kKVT;
+  const int k1 = min(k0 + kKVT, a.Sk);
+  const bool key_tail = (k0 + kKVT) > a.Sk;
+  const int delta = a.Sk - a.Sq;
+  const int kr_own = kKW * grp + n;          // this lane's key row within the tile
+  const int mykey = k0 + kr_own;             // this lane's key (column of S / dP)
+
+  // The group's K rows (role P) or V rows (role dS) as B fragments (slots d 16kc + 8g
+  // .. +7); role P also stores its K rows into the LDS tile for the dQ product.  Keys
+  // past S_k read as zero.
+  const T* kvbase = reinterpret_cast<const T*>(role_p ? a.k : a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const __amdgpu_buffer_rsrc_t kvrs = make_rsrc(kvbase, (uint32_t)a.Sk * D * 2);
+  V8 bf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const u32x4 x = buf_load_16(kvrs, (uint32_t)(mykey * D + 16 * kc + 8 * g) * 2);
+    bf[kc] = as_v8<V8>(x);
+    if (DQ && role_p) st_lds_16(lds + L::K + kr_own * L::ROWB + (((2 * kc + g) ^ kv_swz<D>(kr_own)) * 16), x);
+  }
+
+  f32x16 acc[DB];                            // dV (role P) or dK (role dS) of the group
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  const ColPlan cp = plan_cols(k0, k1, a.Sq, a.Sk, kKVQ, CAUSAL);
+  const int nq = cp.n_qtiles - cp.first_qtile;
+  const int nsteps = nq * a.group;
+  auto step_coords = [&](int step, int& h, int& qt) {
+    h = kvh * a.group + step / nq;
+    qt = cp.first_qtile + step % nq;
+  };
+
+  // Direct HBM -> LDS staging of one step's Q and dO tiles into slot sb: wave load j
+  // fills LDS bytes [1024 j, 1024 j + 1024) of the tile, i.e. row j 64 / CPR + lane / CPR
+  // at position lane % CPR, which holds global chunk position ^ kv_swz(row).
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  auto stage = [&](int step, int sb) {
+    int h, qt;
+    step_coords(step, h, qt);
+    const int64_t base = ((int64_t)(b * a.Hq + h) * a.Sq) * D;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const T*>(a.q) + base, (uint32_t)a.Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<const T*>(a.dO) + base, (uint32_t)a.Sq * D * 2);
+#pragma unroll
+    for (int j = w; j < WL; j += kKVW) {
+      const int row = j * kWave / CPR + lrow;
+      const uint32_t voff = (uint32_t)((row * D) + 8 * (lpos ^ kv_swz<D>(row))) * 2;
+      const uint32_t soff = (uint32_t)(qt * kKVQ * D * 2);
+      const uint32_t dq = __builtin_amdgcn_readfirstlane(lds_offset(lds + L::Q0 + sb * L::QT + j * kWave * 16));
+      const uint32_t dd = __builtin_amdgcn_readfirstlane(lds_offset(lds + L::DO0 + sb * L::QT + j * kWave * 16));
+      lds_load_16(qr, voff, soff, dq);
+      lds_load_16(dr, voff, soff, dd);
+    }
+  };
+  // LSE (base 2) and D of the step's rows, through registers
+  float pre = 0.f;
+  auto fetch_rows = [&](int step) {
+    if (tid < 2 * kKVQ) {
+      int h, qt;
+      step_coords(step, h, qt);
+      const int qr = qt * kKVQ + (tid & (kKVQ - 1));
+      const int64_t ri = (int64_t)(b * a.Hq + h) * a.Sq + qr;
+      pre = qr < a.Sq ? (tid < kKVQ ? a.lse[ri] * ATTN_LOG2E : a.delta[ri]) : (tid < kKVQ ? INFINITY : 0.f);
+    }
+  };
+  auto store_rows = [&](int sb) {
+    if (tid < kKVQ) s_lse[sb][tid] = pre;
+    else if (tid < 2 * kKVQ) s_del[sb][tid - kKVQ] = pre;
+  };
+
+  // Transpose read of a row-major staged tile: the 16-lane group reads rows r0 .. r0+3
+  // at columns c0 .. c0+15 (lane s addresses row r0 + s/4, columns c0 + 4(s%4) .. +3);
+  // lane i receives column c0 + i of the 4 rows.
+  auto tr_rows = [&](const uint8_t* tile, int r0, int c0) -> u32x2 {
+    const int r = r0 + (s16 >> 2);
+    const int col = c0 + 4 * (s16 & 3);
+    return tr_read(tile + r * L::ROWB + (((col >> 3) ^ kv_swz<D>(r)) * 16) + (col & 7) * 2);
+  };
+  float* phand = reinterpret_cast<float*>(lds + L::P) + grp * 16 * kWave + lane;   // [reg][lane]
+
+  // Phase 1: S (role P) or dP (role dS) for the group's 32 keys: A = Q / dO rows (row n,
+  // chunk 2kc + g) of the staged tile, B = the group's K / V fragments.  Role P turns S
+  // into P (masked) and hands it to its partner.
+  auto phase1 = [&](auto masked_tag, int qt, int sb, f32x16& x) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const uint8_t* src = lds + (role_p ? L::Q0 : L::DO0) + sb * L::QT;
+    x = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const V8 af = as_v8<V8>(ld_lds_16(src + n * L::ROWB + (((2 * kc + g) ^ kv_swz<D>(n)) * 16)));
+      x = E::mfma(af, bf[kc], x);
+    }
+    if (role_p) {
+      // register i holds query 8(i/4) + 4g + i%4 of the step
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&s_lse[sb][8 * j + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          float pv = fast_exp2(fmaf(x[i], a.scale_log2, -lv[e]));
+          if constexpr (MASKED) {
+            const int qr = qt * kKVQ + 8 * j + 4 * g + e;
+            const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
+            pv = vis ? pv : 0.f;
+          }
+          x[i] = pv;
+          phand[i * kWave] = pv;
+        }
+      }
+    }
+  };
+
+  // Phase 2: role P: dV += P^T dO; role dS: dS = P (dP - D), dK += dS^T Q, dS to LDS.
+  // Chunk c: A = registers 8c .. 8c+7 (queries 16c + 4g + s%4 and 16c + 8 + 4g + s%4),
+  // B = dO / Q columns by transpose reads of those rows; bf16 carries P and dS as
+  // hi + lo pairs.
+  auto phase2 = [&](int sb, f32x16& x) {
+    uint8_t* dsv = lds + L::DS + sb * L::DSS;
+    uint8_t* dsr = dsv + L::DSS / 2;
+    const uint8_t* src = lds + (role_p ? L::DO0 : L::Q0) + sb * L::QT;
+    if (!role_p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[sb][8 * j + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          x[i] = phand[i * kWave] * (x[i] - dl[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r0 = 16 * c + 4 * g;
+      u32x4 hi, lo;
+      split_pack4x2<T>(f32x4{x[8 * c + 0], x[8 * c + 1], x[8 * c + 2], x[8 * c + 3]},
+                       f32x4{x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]}, hi, lo);
+      if (DQ && !role_p) {
+        // dS key-major: this lane's key row, queries r0 .. r0+3 and r0+8 .. r0+11
+        st_lds_8(dsv + kv_ds_off(kr_own, r0), u32x2{hi.x, hi.y});
+        st_lds_8(dsv + kv_ds_off(kr_own, r0 + 8), u32x2{hi.z, hi.w});
+        if constexpr (kSplit<T>) {
+          st_lds_8(dsr + kv_ds_off(kr_own, r0), u32x2{lo.x, lo.y});
+          st_lds_8(dsr + kv_ds_off(kr_own, r0 + 8), u32x2{lo.z, lo.w});
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int c0 = 32 * db + 16 * gh;
+        const u32x2 t0 = tr_rows(src, r0, c0), t1 = tr_rows(src, r0 + 8, c0);
+        const V8 bt = as_v8<V8>(u32x4{t0.x, t0.y, t1.x, t1.y});
+        acc[db] = E::mfma(as_v8<V8>(hi), bt, acc[db]);
+        if constexpr (kSplit<T>) acc[db] = E::mfma(as_v8<V8>(lo), bt, acc[db]);
+      }
+    }
+  };
+
+  // Phase 3: dQ = dS K over the tile's 128 keys in 16x16 tiles (16 queries x 16 d): wave w
+  // takes query block w / 4 and TPW adjacent d blocks, so its dS reads serve all of them.
+  // A = dS (lane = query column, slots = keys 32kc + 8G + s%4 and + 4, by transpose reads
+  // of the key-major dS), B = K (lane = d column, same keys, transpose reads of the K
+  // tile).  Result lane = d column, registers = queries 4G + i.
+  constexpr int TPW = DQB / kKVW;            // dQ tiles per wave
+  const int G4 = lane >> 4;
+  auto phase3 = [&](int h, int qt, int sb) {
+    const uint8_t* dsv = lds + L::DS + sb * L::DSS;
+    const uint8_t* dsr = dsv + L::DSS / 2;
+    float* dqb = a.dq_acc + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
+    const int tq = w / (kKVW / 2);
+    const int db0 = (w % (kKVW / 2)) * TPW;
+    f32x4 dq[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) dq[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < kKVT / 32; ++kc) {
+      const int r0 = 32 * kc + 8 * G4;
+      const int qc = 16 * tq + 4 * (s16 & 3);
+      const int kr = r0 + (s16 >> 2);
+      const u32x2 a0 = tr_read(dsv + kv_ds_off(kr, qc)), a1 = tr_read(dsv + kv_ds_off(kr + 4, qc));
+      u32x2 e0 = {0u, 0u}, e1 = {0u, 0u};
+      if constexpr (kSplit<T>) {
+        e0 = tr_read(dsr + kv_ds_off(kr, qc));
+        e1 = tr_read(dsr + kv_ds_off(kr + 4, qc));
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const u32x2 b0 = tr_rows(lds + L::K, r0, 16 * (db0 + t)), b1 = tr_rows(lds + L::K, r0 + 4, 16 * (db0 + t));
+        const u32x4 kb4 = {b0.x, b0.y, b1.x, b1.y};
+        dq[t] = MF::run(u32x4{a0.x, a0.y, a1.x, a1.y}, kb4, dq[t]);
+        if constexpr (kSplit<T>) dq[t] = MF::run(u32x4{e0.x, e0.y, e1.x, e1.y}, kb4, dq[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int dcol = 16 * (db0 + t) + s16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qr = qt * kKVQ + 16 * tq + 4 * G4 + i;
+        if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, dq[t][i]);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    stage(0, 0);
+    fetch_rows(0);
+  }
+  // With DQ one more pass runs the last step's dQ tiles.
+  const int npass = (DQ && nsteps > 0) ? nsteps + 1 : nsteps;
+  int ph = 0, pqt = 0;                       // the previous step's head and query tile
+  for (int step = 0; step < npass; ++step) {
+    const bool work = step < nsteps;
+    int h = 0, qt = 0;
+    if (work) step_coords(step, h, qt);
+    const int sb = step & 1;
+    if (work) store_rows(sb);
+    // this step's tiles have landed (own loads) and, after the barrier, everyone's;
+    // every wave has finished step - 1 (its P handoff, its dS writes, and the staged
+    // slot the loads below overwrite)
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (step + 1 < nsteps) {
+      stage(step + 1, sb ^ 1);
+      fetch_rows(step + 1);
+    }
+    if constexpr (DQ) {
+      if (step > 0) phase3(ph, pqt, sb ^ 1);
+    }
+    if (work) {
+      const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
+      f32x16 x;
+      if (masked)
+        phase1(std::true_type{}, qt, sb, x);
+      else
+        phase1(std::false_type{}, qt, sb, x);
+      __syncthreads();                       // P of every group visible
+      phase2(sb, x);
+    }
+    ph = h;
+    pqt = qt;
+  }
+  wait_vmcnt<0>();
+
+  // dV = sum P^T dO (role P), dK = scale sum dS^T Q (role dS); lane = d column 32db + n,
+  // register i = key 8(i/4) + 4g + i%4 of the group's 32
+  G* out = reinterpret_cast<G*>(role_p ? a.dv : a.dk) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
+  const float f = role_p ? 1.f : a.scale;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + kKW * grp + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (key < a.Sk) store_grad<G>(out + (int64_t)key * D + 32 * db + n, acc[db][i] * f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // 4. Deterministic dQ: the query-row owner ("M4.4 - FlashAttention-2 ...", section
 // 0x06.1G and its ownership table: with queries as the owner, dQ_i is a direct output).
 // One workgroup owns a 128-row query tile of one (b, h_q) and one of dq_splits
@@ -814,11 +1161,14 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
+  const dim3 gkv((unsigned)((a.Sk + kKVT - 1) / kKVT), (unsigned)(a.B * a.Hkv));
   if (a.deterministic) {
     if (a.dropout)
       main_k<T, G, D, false, true>(a, grid, stream);
+    else if (a.causal)
+      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, false>), gkv, dim3(kKVW * kWave), 0, stream, a);
     else
-      main_k<T, G, D, false, false>(a, grid, stream);
+      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, false>), gkv, dim3(kKVW * kWave), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
@@ -841,8 +1191,10 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   }
   if (a.dropout)
     main_k<T, G, D, true, true>(a, grid, stream);
+  else if (a.causal)
+    hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, true>), gkv, dim3(kKVW * kWave), 0, stream, a);
   else
-    main_k<T, G, D, true, false>(a, grid, stream);
+    hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, true>), gkv, dim3(kKVW * kWave), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_convert_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
