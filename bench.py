@@ -59,10 +59,11 @@ def _log(*a):
 SETTLE_S = 0.2
 
 
-def _settle(fn, torch, seconds=SETTLE_S):
-    """Untimed launches of ``fn`` for about ``seconds`` of wall time, so that the GPU runs
-    at its working clock when the warm-up and the timed launches start (after the host
-    work between workloads the first launches run at a lower clock)."""
+def _settle(fn, torch, seconds=None):
+    """Untimed launches of ``fn`` for about ``seconds`` (SETTLE_S) of wall time, so that
+    the GPU runs at its working clock when the warm-up and the timed launches start
+    (after the host work between workloads the first launches run at a lower clock)."""
+    seconds = SETTLE_S if seconds is None else seconds
     t0 = time.perf_counter()
     n = 0
     while time.perf_counter() - t0 < seconds:
@@ -351,10 +352,15 @@ def main():
     ap.add_argument("--only", default=None, help="run only this extra workload (" + ", ".join(EXTRA) + ")")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the clock-settling launches (counter-collection runs, where timing is not used)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="first run one 256 MiB device-to-device copy (known bytes) to calibrate "
                          "the byte counters of a profiler run")
     args = ap.parse_args()
+    global SETTLE_S
+    if args.no_settle:
+        SETTLE_S = 0.0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the kernels run on a single MI355X)", file=sys.stderr)
