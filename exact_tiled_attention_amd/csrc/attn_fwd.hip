@@ -501,10 +501,14 @@ void fwd_kernel(FwdArgs a) {
       for (int j = 0; j < QB; ++j) p[j] = probs_chunk(cur[j], cc, m_use[j], l0[j], l1[j], t, j, plo[j]);
     };
     if (has_cur && has_nxt) {
-      // steady state: one basic block, chunk by chunk
+      // steady state: one basic block, chunk by chunk.  The wave issues the next
+      // tile's score MFMAs at raised priority, so that with several waves per SIMD the
+      // matrix core gets its work ahead of the other waves' vector work.
 #pragma unroll
       for (int cc = 0; cc < PC; ++cc) {
+        __builtin_amdgcn_s_setprio(1);
         score_part(nxt, (i + 1) % DEPTH, cc * KPC, (cc + 1) * KPC);
+        __builtin_amdgcn_s_setprio(0);
         u32x4 p[QB], plo[QB];
         probs(cc, p, plo);
         pv_chunk(p, plo, i % DEPTH, cc);
