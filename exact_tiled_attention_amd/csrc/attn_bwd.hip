@@ -170,15 +170,13 @@ __device__ inline void split_pack4x2(const f32x4& x0, const f32x4& x1, u32x4& hi
   }
 }
 
-// 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
+// 8 E4M3 codes -> 8 bf16 values, one instruction per pair (exact: every E4M3 value is
+// a bf16 value, and the conversion's scale is 1).
 __device__ inline u32x4 e4m3x8_bf16(const u32x2& w) {
-  typedef __attribute__((ext_vector_type(2))) float f32x2;
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-  return u32x4{Elem<bf16>::pack2(a[0], a[1]), Elem<bf16>::pack2(b[0], b[1]), Elem<bf16>::pack2(c[0], c[1]),
-               Elem<bf16>::pack2(d[0], d[1])};
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, true))};
 }
 
 // DQ: also add dS K into the float32 dQ accumulator (atomics); without it the kernel

@@ -54,18 +54,14 @@ __device__ inline f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// 8 E4M3 bytes (two dwords) -> 8 bf16 values (exact).
+// 8 E4M3 bytes (two dwords) -> 8 bf16 values, one instruction per pair (exact: every
+// E4M3 value is a bf16 value, and the conversion's scale is 1).
 __device__ inline u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
-  typedef __attribute__((ext_vector_type(2))) float f32x2;
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
   u32x4 r;
-  r.x = Elem<bf16>::pack2(a[0], a[1]);
-  r.y = Elem<bf16>::pack2(b[0], b[1]);
-  r.z = Elem<bf16>::pack2(c[0], c[1]);
-  r.w = Elem<bf16>::pack2(d[0], d[1]);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.f, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.f, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.f, true));
   return r;
 }
 
@@ -297,6 +293,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         for (int i = 0; i < 16; ++i) o[db][i] *= beta;
       }
     }
+    // A zero-valued tile adds nothing in the current frame (dv is the same in every lane).
+    if (v_zero) return;
     // P^T as the fp8 B operand: slot j = register (j % 16) of key block j / 16.
     i32x8 pb;
 #pragma unroll
@@ -305,7 +303,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       const int i0 = 4 * (wd & 3);
       int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[kbk][i0], s[kbk][i0 + 1], 0, false);
       v = __builtin_amdgcn_cvt_pk_fp8_f32(s[kbk][i0 + 2], s[kbk][i0 + 3], v, true);
-      pb[wd] = v_zero ? 0 : v;     // a zero-valued tile adds nothing in the current frame
+      pb[wd] = v;
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
