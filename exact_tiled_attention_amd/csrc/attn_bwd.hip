@@ -13,7 +13,12 @@
 //      fixed order);
 //   3. convert: dQ = scale * accumulator in the requested gradient type.
 //
-// Wave layout of the main kernel: 8 waves, BKV = 128 keys, wave w owns keys
+// Two column owners implement step 2.  bwd_kv_kernel (further below) splits each
+// 32-key group's work between a P wave and a dS wave on the 32x32x16 matrix core; it
+// serves the plain and fp8 backwards and the deterministic path's dK / dV.
+// bwd_main_kernel, described here, serves the dropout backward.
+//
+// Wave layout of bwd_main_kernel: 8 waves, BKV = 128 keys, wave w owns keys
 // 16w .. 16w+15 of the tile, on the 16x16x32 matrix core (A lane l = row l%16,
 // contraction slots from group l/16; B lane l = column l%16, same slots; C lane l =
 // column l%16, rows 4(l/16) .. +3).  Sixteen keys per wave keep each wave's dK and
@@ -183,13 +188,7 @@ __device__ inline u32x4 e4m3x8_bf16(const u32x2& w) {
 // produces dK and dV only (deterministic mode computes dQ in bwd_dq_kernel).
 // DROP: regenerate the forward's dropout decisions Z (keep / (1 - p)) and use
 // dV += (P Z)^T dO, dS = P (Z dP - D).
-// F8 (T = bf16): Q, K, V are E4M3 codes with per-128-row float32 descales, widened
-// exactly to bf16 in LDS; the gradients are those of attention on the dequantised
-// operands Q_d = dQ Q8, K_d = dK K8, V_d = dV V8.  A 128-key tile is one descale block
-// and a 32-query step lies in one, so the descales are per-step and per-workgroup
-// scalars: S = (scale dQ dK) Q8 K8^T, dP = dV (dO V8^T), dK_d = scale sum (dQ dS)^T Q8,
-// dQ_d = scale dK sum dS K8, dV_d = P^T dO.
-template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool DROP, bool F8 = false>
+template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool DROP>
 __global__ __launch_bounds__(kNTM) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_main_kernel(BwdArgs a) {
   typedef M16<T> MF;
@@ -231,18 +230,10 @@ void bwd_main_kernel(BwdArgs a) {
   const bool key_tail = (k0 + kBKV) > a.Sk;
   const int delta = a.Sk - a.Sq;
 
-  constexpr int EB = F8 ? 1 : 2;            // bytes per stored Q / K / V element
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * EB;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * EB;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)a.Sk * D * EB);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)a.Sk * D * EB);
-  // fp8: this workgroup's key and value descales (its 128 keys are one scale block)
-  float dk_s = 1.f, dv_s = 1.f;
-  if constexpr (F8) {
-    const int nkb = (a.Sk + kBKV - 1) / kBKV;
-    dk_s = a.k_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
-    dv_s = a.v_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
-  }
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * 2;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)a.Sk * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)a.Sk * D * 2);
 
   // The K and V tiles, row-major, in LDS (keys past S_k read as zero): the B operands
   // of S and dP (column = key, slots d 32kc + 8g ..) and the K operand of dQ.
@@ -252,15 +243,10 @@ void bwd_main_kernel(BwdArgs a) {
     for (int r = 0; r < KCH; ++r) {
       const int idx = r * kNTM + tid;
       const int row = idx / CPR;
-      const uint32_t src = (uint32_t)((k0 + row) * D + 8 * (idx % CPR)) * EB;
+      const uint32_t src = (uint32_t)((k0 + row) * D + 8 * (idx % CPR)) * 2;
       const int dst = row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16);
-      if constexpr (F8) {
-        st_lds_16(lds + L::K + dst, e4m3x8_bf16(buf_load_8(krs, src)));
-        st_lds_16(lds + L::V + dst, e4m3x8_bf16(buf_load_8(vrs, src)));
-      } else {
-        st_lds_16(lds + L::K + dst, buf_load_16(krs, src));
-        st_lds_16(lds + L::V + dst, buf_load_16(vrs, src));
-      }
+      st_lds_16(lds + L::K + dst, buf_load_16(krs, src));
+      st_lds_16(lds + L::V + dst, buf_load_16(vrs, src));
     }
   }
 
@@ -281,7 +267,6 @@ void bwd_main_kernel(BwdArgs a) {
   const int st_t = tid % (kNTM / 2);
   u32x4 sreg[SCH];
   float slse = 0.f, sdel = 0.f;
-  const int nqb = (a.Sq + kBKV - 1) / kBKV;   // fp8: query descale blocks per head
 
   auto step_coords = [&](int step, int& h, int& qt) {
     h = kvh * a.group + step / nq;
@@ -290,20 +275,13 @@ void bwd_main_kernel(BwdArgs a) {
   auto prefetch = [&](int step) {
     int h, qt;
     step_coords(step, h, qt);
-    // fp8: Q holds one-byte codes (widened when staged), dO 16-bit values
-    const int eb = (F8 && !stage_do) ? 1 : 2;
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(stage_do ? a.dO : a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D * eb;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * eb);
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(stage_do ? a.dO : a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D * 2;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * 2);
 #pragma unroll
     for (int r = 0; r < SCH; ++r) {
       const int idx = r * (kNTM / 2) + st_t;
       const uint32_t off = (uint32_t)((qt * BQ + idx / CPR) * D + 8 * (idx % CPR));
-      if (F8 && !stage_do) {
-        const u32x2 c8 = buf_load_8(rs, off);
-        sreg[r] = u32x4{c8.x, c8.y, 0u, 0u};
-      } else {
-        sreg[r] = buf_load_16(rs, off * 2);
-      }
+      sreg[r] = buf_load_16(rs, off * 2);
     }
     if (tid < BQ) {
       const int qr = qt * BQ + tid;
@@ -318,8 +296,7 @@ void bwd_main_kernel(BwdArgs a) {
     for (int r = 0; r < SCH; ++r) {
       const int idx = r * (kNTM / 2) + st_t;
       const int row = idx / CPR;
-      const u32x4 val = (F8 && !stage_do) ? e4m3x8_bf16(u32x2{sreg[r].x, sreg[r].y}) : sreg[r];
-      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), val);
+      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), sreg[r]);
     }
     if (tid < BQ) {
       s_lse[sb][tid] = slse;
@@ -345,13 +322,6 @@ void bwd_main_kernel(BwdArgs a) {
   // MASKED applies the element mask (tails and the causal band).
   auto compute = [&](auto masked_tag, int qt, int h, int sb) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    // fp8: the step's query descale (its 32 rows lie in one 128-row block); the score
-    // factor takes dQ dK, the dK product takes dQ through dS
-    float dq_s = 1.f, sl2 = a.scale_log2;
-    if constexpr (F8) {
-      dq_s = a.q_scale[(int64_t)(b * a.Hq + h) * nqb + (qt * BQ) / kBKV];
-      sl2 = a.scale_log2 * dq_s * dk_s;
-    }
     // Dropout decisions, first (their temporaries never meet the products' registers),
     // as bit 4t + i for query 16t + 4g + i.  The lane's key is mykey; the four lanes of a
     // key quad (n = 4a .. 4a+3) share the Philox counter word mykey / 4, so each computes
@@ -406,7 +376,7 @@ void bwd_main_kernel(BwdArgs a) {
       const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[sb][qb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float pv = fast_exp2(fmaf(s[t][i], sl2, -lv[i]));
+        float pv = fast_exp2(fmaf(s[t][i], a.scale_log2, -lv[i]));
         if constexpr (MASKED) {
           const int qr = qt * BQ + qb + i;
           const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
@@ -417,7 +387,7 @@ void bwd_main_kernel(BwdArgs a) {
           z = ((keepbits >> (4 * t + i)) & 1u) ? a.drop.rp : 0.f;
         }
         s[t][i] = pv * z;
-        dp[t][i] = pv * (z * (F8 ? dv_s * dp[t][i] : dp[t][i]) - dl[i]);
+        dp[t][i] = pv * (z * dp[t][i] - dl[i]);
       }
     }
     // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries 4g + i and
@@ -426,10 +396,7 @@ void bwd_main_kernel(BwdArgs a) {
     // bits), so these two sums keep float32-like precision.
     u32x4 pp, pl, ss, sl;
     split_pack4x2<T>(s[0], s[1], pp, pl);
-    if constexpr (F8)
-      split_pack4x2<T>(dp[0] * dq_s, dp[1] * dq_s, ss, sl);
-    else
-      split_pack4x2<T>(dp[0], dp[1], ss, sl);
+    split_pack4x2<T>(dp[0], dp[1], ss, sl);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const u32x2 olo = tr_tile(sdo, 4 * g, 16 * db), ohi = tr_tile(sdo, 16 + 4 * g, 16 * db);
@@ -518,7 +485,7 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int qr = qt * BQ + 16 * tq + 4 * g + i;
-          if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, F8 ? acc[i] * dk_s : acc[i]);
+          if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, acc[i]);
         }
       }
     }
@@ -595,7 +562,13 @@ __device__ inline int kv_ds_off(int key, int q) {
   return key * (kKVQ * 2) + ((u ^ (2 * ((key >> 1) & 1))) * 16) + (q & 7) * 2;
 }
 
-template <typename T, typename G, int D, bool CAUSAL, bool DQ>
+// F8 (T = bf16, with DQ): Q, K, V are E4M3 codes with per-128-row float32 descales,
+// widened exactly to bf16; a 128-key tile is one descale block and a 32-query step lies
+// in one, so S = (scale dQ dK) Q8 K8^T, dP = dV (dO V8^T), dK_d = scale sum (dQ dS)^T Q8,
+// dQ_d = scale dK sum dS K8 and dV_d = P^T dO.  The Q tile is loaded into registers at
+// the start of a step and widened into its LDS slot at the end (dO still goes straight
+// to LDS).
+template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool F8 = false>
 __global__ __launch_bounds__(kKVW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdArgs a) {
   typedef Elem<T> E;
@@ -641,12 +614,24 @@ void bwd_kv_kernel(BwdArgs a) {
   // The group's K rows (role P) or V rows (role dS) as B fragments (slots d 16kc + 8g
   // .. +7); role P also stores its K rows into the LDS tile for the dQ product.  Keys
   // past S_k read as zero.
-  const T* kvbase = reinterpret_cast<const T*>(role_p ? a.k : a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const __amdgpu_buffer_rsrc_t kvrs = make_rsrc(kvbase, (uint32_t)a.Sk * D * 2);
+  constexpr int EB = F8 ? 1 : 2;             // bytes per stored Q / K / V element
+  const uint8_t* kvbase = reinterpret_cast<const uint8_t*>(role_p ? a.k : a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * EB;
+  const __amdgpu_buffer_rsrc_t kvrs = make_rsrc(kvbase, (uint32_t)a.Sk * D * EB);
+  // fp8: this workgroup's key and value descales (its 128 keys are one scale block)
+  float dk_s = 1.f, dv_s = 1.f;
+  if constexpr (F8) {
+    const int nkb = (a.Sk + kKVT - 1) / kKVT;
+    dk_s = a.k_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
+    dv_s = a.v_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
+  }
   V8 bf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    const u32x4 x = buf_load_16(kvrs, (uint32_t)(mykey * D + 16 * kc + 8 * g) * 2);
+    u32x4 x;
+    if constexpr (F8)
+      x = e4m3x8_bf16(buf_load_8(kvrs, (uint32_t)(mykey * D + 16 * kc + 8 * g)));
+    else
+      x = buf_load_16(kvrs, (uint32_t)(mykey * D + 16 * kc + 8 * g) * 2);
     bf[kc] = as_v8<V8>(x);
     if (DQ && role_p) st_lds_16(lds + L::K + kr_own * L::ROWB + (((2 * kc + g) ^ kv_swz<D>(kr_own)) * 16), x);
   }
@@ -667,11 +652,15 @@ void bwd_kv_kernel(BwdArgs a) {
   // fills LDS bytes [1024 j, 1024 j + 1024) of the tile, i.e. row j 64 / CPR + lane / CPR
   // at position lane % CPR, which holds global chunk position ^ kv_swz(row).
   const int lrow = lane / CPR, lpos = lane % CPR;
+  // fp8: the step's Q codes, 8 per thread (chunk tid of the 32 x D tile), loaded by
+  // stage() and widened into the LDS slot by store_q()
+  constexpr int Q8C = kKVQ * D / 8;          // 8-byte chunks of a Q8 tile
+  u32x2 q8 = {0u, 0u};
   auto stage = [&](int step, int sb) {
     int h, qt;
     step_coords(step, h, qt);
     const int64_t base = ((int64_t)(b * a.Hq + h) * a.Sq) * D;
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const T*>(a.q) + base, (uint32_t)a.Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const uint8_t*>(a.q) + base * EB, (uint32_t)a.Sq * D * EB);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<const T*>(a.dO) + base, (uint32_t)a.Sq * D * 2);
 #pragma unroll
     for (int j = w; j < WL; j += kKVW) {
@@ -680,9 +669,25 @@ void bwd_kv_kernel(BwdArgs a) {
       const uint32_t soff = (uint32_t)(qt * kKVQ * D * 2);
       const uint32_t dq = __builtin_amdgcn_readfirstlane(lds_offset(lds + L::Q0 + sb * L::QT + j * kWave * 16));
       const uint32_t dd = __builtin_amdgcn_readfirstlane(lds_offset(lds + L::DO0 + sb * L::QT + j * kWave * 16));
-      lds_load_16(qr, voff, soff, dq);
+      if constexpr (!F8) lds_load_16(qr, voff, soff, dq);
       lds_load_16(dr, voff, soff, dd);
     }
+    if constexpr (F8) {
+      if (tid < Q8C) q8 = buf_load_8(qr, (uint32_t)((qt * kKVQ + tid / (D / 8)) * D + 8 * (tid % (D / 8))));
+    }
+  };
+  auto store_q = [&](int sb) {
+    if constexpr (F8) {
+      if (tid < Q8C) {
+        const int row = tid / (D / 8), c = tid % (D / 8);
+        st_lds_16(lds + L::Q0 + sb * L::QT + row * L::ROWB + ((c ^ kv_swz<D>(row)) * 16), e4m3x8_bf16(q8));
+      }
+    }
+  };
+  // fp8: the query descale of a step (its 32 rows lie in one 128-row block)
+  const int nqb = (a.Sq + kKVT - 1) / kKVT;
+  auto q_descale = [&](int h, int qt) {
+    return F8 ? a.q_scale[(int64_t)(b * a.Hq + h) * nqb + (qt * kKVQ) / kKVT] : 1.f;
   };
   // LSE (base 2) and D of the step's rows, through registers
   float pre = 0.f;
@@ -713,7 +718,7 @@ void bwd_kv_kernel(BwdArgs a) {
   // Phase 1: S (role P) or dP (role dS) for the group's 32 keys: A = Q / dO rows (row n,
   // chunk 2kc + g) of the staged tile, B = the group's K / V fragments.  Role P turns S
   // into P (masked) and hands it to its partner.
-  auto phase1 = [&](auto masked_tag, int qt, int sb, f32x16& x) {
+  auto phase1 = [&](auto masked_tag, int qt, int sb, float sl2, f32x16& x) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const uint8_t* src = lds + (role_p ? L::Q0 : L::DO0) + sb * L::QT;
     x = f32x16{};
@@ -730,7 +735,7 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
-          float pv = fast_exp2(fmaf(x[i], a.scale_log2, -lv[e]));
+          float pv = fast_exp2(fmaf(x[i], sl2, -lv[e]));
           if constexpr (MASKED) {
             const int qr = qt * kKVQ + 8 * j + 4 * g + e;
             const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
@@ -747,7 +752,7 @@ void bwd_kv_kernel(BwdArgs a) {
   // Chunk c: A = registers 8c .. 8c+7 (queries 16c + 4g + s%4 and 16c + 8 + 4g + s%4),
   // B = dO / Q columns by transpose reads of those rows; bf16 carries P and dS as
   // hi + lo pairs.
-  auto phase2 = [&](int sb, f32x16& x) {
+  auto phase2 = [&](int sb, float dq_s, f32x16& x) {
     uint8_t* dsv = lds + L::DS + sb * L::DSS;
     uint8_t* dsr = dsv + L::DSS / 2;
     const uint8_t* src = lds + (role_p ? L::DO0 : L::Q0) + sb * L::QT;
@@ -758,7 +763,7 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
-          x[i] = phand[i * kWave] * (x[i] - dl[e]);
+          x[i] = phand[i * kWave] * ((F8 ? dv_s * x[i] : x[i]) - dl[e]);
         }
       }
     }
@@ -776,6 +781,12 @@ void bwd_kv_kernel(BwdArgs a) {
           st_lds_8(dsr + kv_ds_off(kr_own, r0), u32x2{lo.x, lo.y});
           st_lds_8(dsr + kv_ds_off(kr_own, r0 + 8), u32x2{lo.z, lo.w});
         }
+      }
+      if constexpr (F8) {
+        // the dK product takes dS dQ (the stored dS stays unscaled for dQ)
+        if (!role_p)
+          split_pack4x2<T>(f32x4{x[8 * c + 0], x[8 * c + 1], x[8 * c + 2], x[8 * c + 3]} * dq_s,
+                           f32x4{x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]} * dq_s, hi, lo);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
@@ -829,13 +840,14 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int qr = qt * kKVQ + 16 * tq + 4 * G4 + i;
-        if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, dq[t][i]);
+        if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, F8 ? dq[t][i] * dk_s : dq[t][i]);
       }
     }
   };
 
   if (nsteps > 0) {
     stage(0, 0);
+    store_q(0);
     fetch_rows(0);
   }
   // With DQ one more pass runs the last step's dQ tiles.
@@ -861,14 +873,17 @@ void bwd_kv_kernel(BwdArgs a) {
     }
     if (work) {
       const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
+      const float dq_s = q_descale(h, qt);
+      const float sl2 = F8 ? a.scale_log2 * dq_s * dk_s : a.scale_log2;
       f32x16 x;
       if (masked)
-        phase1(std::true_type{}, qt, sb, x);
+        phase1(std::true_type{}, qt, sb, sl2, x);
       else
-        phase1(std::false_type{}, qt, sb, x);
+        phase1(std::false_type{}, qt, sb, sl2, x);
       __syncthreads();                       // P of every group visible
-      phase2(sb, x);
+      phase2(sb, dq_s, x);
     }
+    if (step + 1 < nsteps) store_q(sb ^ 1);  // fp8: the next step's Q, widened
     ph = h;
     pqt = qt;
   }
@@ -1146,20 +1161,20 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.Sk + kBKV - 1) / kBKV), (unsigned)(a.B * a.Hkv));
   const int64_t n4 = rows * D / 4;
+  const dim3 gkv((unsigned)((a.Sk + kKVT - 1) / kKVT), (unsigned)(a.B * a.Hkv));
   if constexpr (std::is_same<T, bf16>::value) {
     if (a.fp8) {
-      // E4M3 operands: the atomic-dQ column owner only
+      // E4M3 operands: the split-role column owner with atomic dQ
       if (a.causal)
-        hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, true, false, true>), grid, dim3(kNTM), 0, stream, a);
+        hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, true, true>), gkv, dim3(kKVW * kWave), 0, stream, a);
       else
-        hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, true, false, true>), grid, dim3(kNTM), 0, stream, a);
+        hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, true, true>), gkv, dim3(kKVW * kWave), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((bwd_convert_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
       return hipGetLastError();
     }
   }
-  const dim3 gkv((unsigned)((a.Sk + kKVT - 1) / kKVT), (unsigned)(a.B * a.Hkv));
   if (a.deterministic) {
     if (a.dropout)
       main_k<T, G, D, false, true>(a, grid, stream);
