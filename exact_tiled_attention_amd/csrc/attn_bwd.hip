@@ -13,26 +13,16 @@
 //      fixed order);
 //   3. convert: dQ = scale * accumulator in the requested gradient type.
 //
-// Two column owners implement step 2.  bwd_kv_kernel (further below) splits each
-// 32-key group's work between a P wave and a dS wave on the 32x32x16 matrix core; it
-// serves the plain and fp8 backwards and the deterministic path's dK / dV.
-// bwd_main_kernel, described here, serves the dropout backward.
-//
-// Wave layout of bwd_main_kernel: 8 waves, BKV = 128 keys, wave w owns keys
-// 16w .. 16w+15 of the tile, on the 16x16x32 matrix core (A lane l = row l%16,
-// contraction slots from group l/16; B lane l = column l%16, same slots; C lane l =
-// column l%16, rows 4(l/16) .. +3).  Sixteen keys per wave keep each wave's dK and
-// dV accumulators at 64 registers, so two waves share each SIMD.  S and dP are
-// computed with the queries (two 16-row tiles of the 32-query step) as M and the
-// wave's keys as N, so each lane holds ONE key and 4 + 4 query rows of it: the
-// A-operand shape of dV += P^T dO and dK += dS^T Q (slots = queries 4g+i and
-// 16+4g+i).  Their B operands (dO and Q with the query index as the contraction) come
-// from the row-major staged tiles through ds_read_b64_tr_b16 (one column of 4
-// consecutive rows per lane).  dQ needs dS with queries as rows: dS goes to LDS
-// key-major (8-byte writes of 4 queries) and comes back through the same transpose
-// read, against K (row-major in LDS, transpose-read with keys as the contraction).
-// Staged rows are unpadded, their 16-byte chunks XOR-swizzled so that the 16-byte
-// fragment reads and the transpose reads of a tile both hit distinct banks.
+// Wave layout of the column owner (bwd_kv_kernel, section 2 below): each 32-key group
+// of the 128-key tile is served by a P wave and a dS wave on the 32x32x16 matrix core.
+// S and dP are computed with the step's queries as M and the group's keys as N, so
+// each lane holds ONE key: the A-operand shape of dV += P^T dO and dK += dS^T Q.  Their
+// B operands (dO and Q with the query index as the contraction) come from the row-major
+// staged tiles through ds_read_b64_tr_b16 (one column of 4 consecutive rows per lane).
+// dQ needs dS with queries as rows: dS goes to LDS key-major and comes back through the
+// same transpose read, against K (row-major in LDS).  Staged rows are unpadded, their
+// 16-byte chunks XOR-swizzled so that the fragment reads and the transpose reads of a
+// tile both hit distinct banks.
 #include <type_traits>
 
 #include "../../include/attn.h"
@@ -45,8 +35,6 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kNT = 256;      // preprocess / convert kernels
-constexpr int kNTM = 512;     // main kernel: 8 waves
-constexpr int kBKV = 128;
 
 // ---------------------------------------------------------------------------------
 // 1. D = rowsum(dO * O) and dQ accumulator clear.  One row per LPR lanes.
@@ -99,36 +87,6 @@ template <typename G> __device__ inline void store_grad(G* p, float x) { *p = (G
 // bf16 keeps 8 significant bits; P and dS feed the dV / dK sums as hi + lo pairs.
 template <typename T> constexpr bool kSplit = false;
 template <> constexpr bool kSplit<bf16> = true;
-
-// ---------------------------------------------------------------------------------
-// 2. main column-owner kernel
-//
-// Chunk swizzle of rows staged in LDS (16-byte chunk p of row r at p ^ swz(r)).  The
-// tiles are read as 16x16x32 fragments (16 consecutive rows at four consecutive chunks
-// per wave) and by transpose reads (8 rows x 2 chunks per 32 lanes).  d = 128: the
-// identity on the row's low four bits; the hardware's conflict counter reads 0 for the
-// fragment reads and 2-way for the transpose reads, against 2-way fragment reads and
-// conflict-free transpose reads for 2(r mod 8) + bit 3 (a wave reads 24 KB of
-// fragments and 16 KB by transpose reads per step; the causal GQA [2,32,8192,128] column
-// owner takes 10 % fewer cycles).  Rows of 128 bytes (d = 64)
-// pair up in one 256-byte bank span.
-template <int D> __device__ inline int swz_row(int r) {
-  if constexpr (D == 128) return r & 15;
-  return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-}
-
-template <int D>
-struct BwdLds {
-  static constexpr int BQ = 32;               // queries per step
-  static constexpr int ROWB = D * 2;          // staged row bytes
-  static constexpr int Q = 0;                 // byte offsets
-  static constexpr int DO = Q + BQ * ROWB;
-  static constexpr int DST = DO + BQ * ROWB;  // dS^T [key][query], 16-bit, 64-byte rows
-  static constexpr int DSL = DST + kBKV * BQ * 2; // its bf16 residual (same layout)
-  static constexpr int K = DSL + kBKV * BQ * 2;   // K tile, row-major
-  static constexpr int V = K + kBKV * ROWB;       // V tile, row-major
-  static constexpr int BYTES = V + kBKV * ROWB;
-};
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -184,332 +142,8 @@ __device__ inline u32x4 e4m3x8_bf16(const u32x2& w) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.f, true))};
 }
 
-// DQ: also add dS K into the float32 dQ accumulator (atomics); without it the kernel
-// produces dK and dV only (deterministic mode computes dQ in bwd_dq_kernel).
-// DROP: regenerate the forward's dropout decisions Z (keep / (1 - p)) and use
-// dV += (P Z)^T dO, dS = P (Z dP - D).
-template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool DROP>
-__global__ __launch_bounds__(kNTM) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_main_kernel(BwdArgs a) {
-  typedef M16<T> MF;
-  typedef BwdLds<D> L;
-  constexpr int BQ = L::BQ;
-  constexpr int KC = D / 32;                // contraction chunks of 32 over d
-  constexpr int DB = D / 16;                // 16-wide d blocks of dK / dV / dQ
-  constexpr int CPR = D / 8;                // 16-byte chunks per row
-  constexpr int SCH = BQ * CPR / (kNTM / 2);   // staging chunks per thread (Q or dO)
-  constexpr int KCH = kBKV * CPR / kNTM;       // K-tile chunks per thread
-  static_assert(SCH >= 1 && SCH * (kNTM / 2) == BQ * CPR, "staging chunks split evenly");
-
-  __shared__ __attribute__((aligned(16))) uint8_t lds[L::BYTES];
-  // Staged Q / dO tiles and their rows' LSE and D: one buffer with dQ (whose dS^T
-  // staging needs the second barrier of each step anyway), two without, the second in
-  // the dS^T region that only the dQ product uses.
-  __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
-  __shared__ __attribute__((aligned(16))) float s_del[2][BQ];
-  static_assert(DQ || 2 * BQ * L::ROWB <= L::K - L::DST, "second stage fits the dS^T region");
-  auto stage_base = [](int sb) { return sb ? L::DST : L::Q; };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int n = lane & 15;
-  const int g = lane >> 4;
-
-  // Workgroups are dispatched in linear order; the key tile varies slowest so that the
-  // tiles with the most visible query tiles under causal masking (the first ones) start
-  // first and the short ones fill the end (longest first).
-  const int nbkv = a.B * a.Hkv;
-  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
-  const int jt = lin / nbkv;                 // key tile
-  const int bkv = lin - jt * nbkv;
-  const int b = bkv / a.Hkv;
-  const int kvh = bkv - b * a.Hkv;
-  const int k0 = jt * kBKV;
-  const int k1 = min(k0 + kBKV, a.Sk);
-  const bool key_tail = (k0 + kBKV) > a.Sk;
-  const int delta = a.Sk - a.Sq;
-
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * 2;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)a.Sk * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)a.Sk * D * 2);
-
-  // The K and V tiles, row-major, in LDS (keys past S_k read as zero): the B operands
-  // of S and dP (column = key, slots d 32kc + 8g ..) and the K operand of dQ.
-  const int mykey = k0 + 16 * w + n;
-  {
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int idx = r * kNTM + tid;
-      const int row = idx / CPR;
-      const uint32_t src = (uint32_t)((k0 + row) * D + 8 * (idx % CPR)) * 2;
-      const int dst = row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16);
-      st_lds_16(lds + L::K + dst, buf_load_16(krs, src));
-      st_lds_16(lds + L::V + dst, buf_load_16(vrs, src));
-    }
-  }
-
-  f32x4 dk[DB], dv[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const ColPlan cp = plan_cols(k0, k1, a.Sq, a.Sk, BQ, CAUSAL);
-  const int nq = cp.n_qtiles - cp.first_qtile;
-  const int nsteps = nq * a.group;
-
-  // Staging: the first half of the threads stages Q, the second dO; chunk idx =
-  // r * 256 + (tid % 256) of the tile is (row idx / CPR, chunk idx % CPR).
-  const bool stage_do = tid >= kNTM / 2;
-  const int st_t = tid % (kNTM / 2);
-  u32x4 sreg[SCH];
-  float slse = 0.f, sdel = 0.f;
-
-  auto step_coords = [&](int step, int& h, int& qt) {
-    h = kvh * a.group + step / nq;
-    qt = cp.first_qtile + step % nq;
-  };
-  auto prefetch = [&](int step) {
-    int h, qt;
-    step_coords(step, h, qt);
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(stage_do ? a.dO : a.q) + ((int64_t)(b * a.Hq + h) * a.Sq) * D * 2;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)a.Sq * D * 2);
-#pragma unroll
-    for (int r = 0; r < SCH; ++r) {
-      const int idx = r * (kNTM / 2) + st_t;
-      const uint32_t off = (uint32_t)((qt * BQ + idx / CPR) * D + 8 * (idx % CPR));
-      sreg[r] = buf_load_16(rs, off * 2);
-    }
-    if (tid < BQ) {
-      const int qr = qt * BQ + tid;
-      const int64_t ri = (int64_t)(b * a.Hq + h) * a.Sq + qr;
-      slse = qr < a.Sq ? a.lse[ri] * ATTN_LOG2E : 0.f;
-      sdel = qr < a.Sq ? a.delta[ri] : 0.f;
-    }
-  };
-  auto store_stage = [&](int sb) {
-    uint8_t* dst = lds + stage_base(sb) + (stage_do ? L::DO - L::Q : 0);
-#pragma unroll
-    for (int r = 0; r < SCH; ++r) {
-      const int idx = r * (kNTM / 2) + st_t;
-      const int row = idx / CPR;
-      st_lds_16(dst + row * L::ROWB + (((idx % CPR) ^ swz_row<D>(row)) * 16), sreg[r]);
-    }
-    if (tid < BQ) {
-      s_lse[sb][tid] = slse;
-      s_del[sb][tid] = sdel;
-    }
-  };
-  // Transpose read of a staged row-major tile: the 16-lane group reads rows rb .. rb+3
-  // at columns c0 .. c0+15 (lane s addresses row rb + s/4, columns c0 + 4(s%4) .. +3);
-  // lane i receives column c0 + i of the 4 rows.
-  auto tr_tile = [&](const uint8_t* tile, int rb, int c0) -> u32x2 {
-    const int r = rb + (n >> 2);
-    const int col = c0 + 4 * (n & 3);
-    return tr_read(tile + r * L::ROWB + (((col >> 3) ^ swz_row<D>(r)) * 16) + (col & 7) * 2);
-  };
-  // dS^T rows are 64 bytes (4 units of 16): unit u of key row r sits at u ^ 2((r>>2)&1),
-  // so the 8 rows x 2 units of one 32-lane transpose-read pass hit distinct banks.
-  auto dst_off = [&](int key, int q) -> int {
-    const int u = q >> 3;
-    return key * (BQ * 2) + ((u ^ (2 * ((key >> 2) & 1))) * 16) + (q & 7) * 2;
-  };
-
-  // One step: S / dP for the wave's keys, P and dS, the dV / dK products, dS^T to LDS.
-  // MASKED applies the element mask (tails and the causal band).
-  auto compute = [&](auto masked_tag, int qt, int h, int sb) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    // Dropout decisions, first (their temporaries never meet the products' registers),
-    // as bit 4t + i for query 16t + 4g + i.  The lane's key is mykey; the four lanes of a
-    // key quad (n = 4a .. 4a+3) share the Philox counter word mykey / 4, so each computes
-    // the call of query (t, n % 4) only and the words move by shuffles: in round r a lane
-    // sends word (n + r) % 4 of its call and receives, from quad lane (n - r) % 4, word
-    // n % 4 (= mykey % 4) of query (t, (n - r) % 4).
-    uint32_t keepbits = 0;
-    if constexpr (DROP) {
-      const int e = n & 3;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qt * BQ + 16 * t + 4 * g + e),
-                                       (uint32_t)(b * a.Hq + h), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int wi = (e + r) & 3;
-          const uint32_t send = wi == 0 ? wv[0] : wi == 1 ? wv[1] : wi == 2 ? wv[2] : wv[3];
-          const uint32_t got = (uint32_t)__shfl((int)send, (lane & ~3) | ((e - r) & 3));
-          keepbits |= (got >= a.drop.thresh ? 1u : 0u) << (4 * t + ((e - r) & 3));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const uint8_t* sq = lds + stage_base(sb);
-    const uint8_t* sdo = sq + (L::DO - L::Q);
-    // S, dP: tile t = query rows 16t .. 16t+15; lane holds queries 16t + 4g + i.  The
-    // K / V fragments of a contraction chunk serve both query tiles.
-    f32x4 s[2], dp[2];
-    const int krow = 16 * w + n;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int koff = krow * L::ROWB + (((4 * kc + g) ^ swz_row<D>(krow)) * 16);
-      const u32x4 bk = ld_lds_16(lds + L::K + koff);
-      const u32x4 bv = ld_lds_16(lds + L::V + koff);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = 16 * t + n;
-        const int off = row * L::ROWB + (((4 * kc + g) ^ swz_row<D>(row)) * 16);
-        const u32x4 aq = ld_lds_16(sq + off);
-        const u32x4 ad = ld_lds_16(sdo + off);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        s[t] = MF::run(aq, bk, kc == 0 ? z : s[t]);
-        dp[t] = MF::run(ad, bv, kc == 0 ? z : dp[t]);
-      }
-      if (D == 128 && (kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
-    }
-    // P = exp2(S log2e scale - LSE log2e); dS = P (dP - D).
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int qb = 16 * t + 4 * g;
-      const f32x4 lv = *reinterpret_cast<const f32x4*>(&s_lse[sb][qb]);
-      const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[sb][qb]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float pv = fast_exp2(fmaf(s[t][i], a.scale_log2, -lv[i]));
-        if constexpr (MASKED) {
-          const int qr = qt * BQ + qb + i;
-          const bool vis = qr < a.Sq && mykey < a.Sk && (!CAUSAL || mykey <= qr + delta);
-          pv = vis ? pv : 0.f;
-        }
-        float z = 1.f;
-        if constexpr (DROP) {
-          z = ((keepbits >> (4 * t + i)) & 1u) ? a.drop.rp : 0.f;
-        }
-        s[t][i] = pv * z;
-        dp[t][i] = pv * (z * dp[t][i] - dl[i]);
-      }
-    }
-    // dV += P^T dO, dK += dS^T Q: A = this lane's key row, slots = queries 4g + i and
-    // 16 + 4g + i; B = dO / Q columns by transpose reads of those rows.  With bf16
-    // elements P and dS enter as hi + lo pairs (x = hi + lo to about 16 significant
-    // bits), so these two sums keep float32-like precision.
-    u32x4 pp, pl, ss, sl;
-    split_pack4x2<T>(s[0], s[1], pp, pl);
-    split_pack4x2<T>(dp[0], dp[1], ss, sl);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const u32x2 olo = tr_tile(sdo, 4 * g, 16 * db), ohi = tr_tile(sdo, 16 + 4 * g, 16 * db);
-      const u32x2 qlo = tr_tile(sq, 4 * g, 16 * db), qhi = tr_tile(sq, 16 + 4 * g, 16 * db);
-      const u32x4 ob = {olo.x, olo.y, ohi.x, ohi.y};
-      const u32x4 qb4 = {qlo.x, qlo.y, qhi.x, qhi.y};
-      dv[db] = MF::run(pp, ob, dv[db]);
-      dk[db] = MF::run(ss, qb4, dk[db]);
-      if (kSplit<T>) {
-        dv[db] = MF::run(pl, ob, dv[db]);
-        dk[db] = MF::run(sl, qb4, dk[db]);
-      }
-      // keep the operand reads of at most two d blocks in flight (registers)
-      if ((db & 1) == 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    // dS^T -> LDS [key][query]: registers 0..3 of tile t are queries 16t + 4g .. +3.
-    uint8_t* dsl = lds + L::DST;
-#pragma unroll
-    for (int t = 0; t < (DQ ? 2 : 0); ++t) {
-      u32x2 pk;
-      pk.x = Elem<T>::pack2(dp[t][0], dp[t][1]);
-      pk.y = Elem<T>::pack2(dp[t][2], dp[t][3]);
-      st_lds_8(dsl + dst_off(krow, 16 * t + 4 * g), pk);
-      if constexpr (kSplit<T>) {   // bf16: the residual dS - hi enters dQ as well
-        u32x2 lo;
-        lo.x = Elem<T>::pack2(dp[t][0] - __builtin_bit_cast(float, pk.x << 16),
-                              dp[t][1] - __builtin_bit_cast(float, pk.x & 0xFFFF0000u));
-        lo.y = Elem<T>::pack2(dp[t][2] - __builtin_bit_cast(float, pk.y << 16),
-                              dp[t][3] - __builtin_bit_cast(float, pk.y & 0xFFFF0000u));
-        st_lds_8(lds + L::DSL + dst_off(krow, 16 * t + 4 * g), lo);
-      }
-    }
-  };
-
-  if (nsteps > 0) prefetch(0);
-  for (int step = 0; step < nsteps; ++step) {
-    int h, qt;
-    step_coords(step, h, qt);
-    // (The first barrier (A) also publishes the K and V tiles.)  With dQ: the previous
-    // step's reads of the staged tiles ended before its barrier (B), and this step's
-    // dS^T writes come after barrier (A): one barrier pair per step.  Without dQ the
-    // stage alternates between two buffers: the one written here was last read in
-    // step - 2, which every wave finished before passing barrier (A) of step - 1, so
-    // one barrier per step suffices.
-    const int sb = DQ ? 0 : (step & 1);
-    store_stage(sb);
-    __syncthreads();                                          // (A) stage visible
-    if (step + 1 < nsteps) prefetch(step + 1);
-
-    const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * BQ > a.Sq;
-    if (masked)
-      compute(std::true_type{}, qt, h, sb);
-    else
-      compute(std::false_type{}, qt, h, sb);
-    if constexpr (DQ) __syncthreads();                        // (B) dS^T visible
-    if constexpr (DQ)
-    // dQ_acc += dS K over the 128 keys: block (query tile tq, d block db) per wave pass;
-    // slots = keys 32kc + 4g + i and 32kc + 16 + 4g + i for both operands (A = dS by
-    // transpose reads of dS^T, B = K by transpose reads of the K tile); result lane =
-    // d column, regs = queries 16tq + 4g + i.
-    {
-      const uint8_t* dsl = lds + L::DST;
-      const uint8_t* kt = lds + L::K;
-      float* dqb = a.dq_acc + ((int64_t)(b * a.Hq + h) * a.Sq) * D;
-      for (int blk = w; blk < 2 * DB; blk += 8) {
-        const int tq = blk / DB;
-        const int db = blk % DB;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < kBKV / 32; ++kc) {
-          const int kb0 = 32 * kc + 4 * g + (n >> 2);
-          const int qcol = 16 * tq + 4 * (n & 3);
-          const u32x2 alo = tr_read(dsl + dst_off(kb0, qcol));
-          const u32x2 ahi = tr_read(dsl + dst_off(kb0 + 16, qcol));
-          const u32x2 blo = tr_tile(kt, 32 * kc + 4 * g, 16 * db);
-          const u32x2 bhi = tr_tile(kt, 32 * kc + 16 + 4 * g, 16 * db);
-          const u32x4 kb4 = {blo.x, blo.y, bhi.x, bhi.y};
-          acc = MF::run(u32x4{alo.x, alo.y, ahi.x, ahi.y}, kb4, acc);
-          if constexpr (kSplit<T>) {
-            const u32x2 rlo = tr_read(lds + L::DSL + dst_off(kb0, qcol));
-            const u32x2 rhi = tr_read(lds + L::DSL + dst_off(kb0 + 16, qcol));
-            acc = MF::run(u32x4{rlo.x, rlo.y, rhi.x, rhi.y}, kb4, acc);
-          }
-        }
-        const int dcol = 16 * db + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qr = qt * BQ + 16 * tq + 4 * g + i;
-          if (qr < a.Sq) unsafeAtomicAdd(dqb + (int64_t)qr * D + dcol, acc[i]);
-        }
-      }
-    }
-  }
-
-  // dK = scale * sum dS^T Q, dV = sum P^T dO; lane = d column, regs = keys 4g + i.
-  G* dkb = reinterpret_cast<G*>(a.dk) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  G* dvb = reinterpret_cast<G*>(a.dv) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int dcol = 16 * db + n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k0 + 16 * w + 4 * g + i;
-      if (key < a.Sk) {
-        store_grad<G>(dkb + (int64_t)key * D + dcol, dk[db][i] * a.scale);
-        store_grad<G>(dvb + (int64_t)key * D + dcol, dv[db][i]);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------------
-// 2b. Column owner with split roles (the plain backward: no dropout, 16-bit operands).
+// 2. Column owner with split roles (every backward: 16-bit or fp8 operands, dropout).
 // One workgroup owns a 128-key tile; four key groups of 32 keys, each served by two
 // waves on one SIMD: wave w (role P) keeps the group's K rows in registers, computes
 // S = Q K^T and P = exp(S - LSE) and accumulates dV += P^T dO; wave w + 4 (role dS)
@@ -543,7 +177,8 @@ struct KvLds {
   static constexpr int DS = K + kKVT * ROWB;        // dS slots 0, 1: [128 keys][32 queries], 64-byte rows
   static constexpr int DSS = 2 * kKVT * kKVQ * 2;   // one slot: the values, then their bf16 residuals
   static constexpr int P = DS + 2 * DSS;            // P handoff [group][16 registers][64 lanes] float32
-  static constexpr int BYTES = P + kKG * 16 * kWave * 4;
+  static constexpr int Z = P + kKG * 16 * kWave * 4; // dropout keep bits [group][64 lanes] uint32
+  static constexpr int BYTES = Z + kKG * kWave * 4;
 };
 
 // Chunk swizzle of staged rows (Q, dO, K): chunk p of row r at position p ^ kv_swz(r).
@@ -568,7 +203,10 @@ __device__ inline int kv_ds_off(int key, int q) {
 // dQ_d = scale dK sum dS K8 and dV_d = P^T dO.  The Q tile is loaded into registers at
 // the start of a step and widened into its LDS slot at the end (dO still goes straight
 // to LDS).
-template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool F8 = false>
+// DROP: regenerate the forward's dropout decisions Z (keep / (1 - p)) and use
+// dV += (P Z)^T dO, dS = P (Z dP - D).  The dS waves draw the step's decisions while the
+// P waves compute probabilities and hand them over through LDS with P's barrier.
+template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool F8 = false, bool DROP = false>
 __global__ __launch_bounds__(kKVW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdArgs a) {
   typedef Elem<T> E;
@@ -714,6 +352,9 @@ void bwd_kv_kernel(BwdArgs a) {
     return tr_read(tile + r * L::ROWB + (((col >> 3) ^ kv_swz<D>(r)) * 16) + (col & 7) * 2);
   };
   float* phand = reinterpret_cast<float*>(lds + L::P) + grp * 16 * kWave + lane;   // [reg][lane]
+  uint32_t* zhand = reinterpret_cast<uint32_t*>(lds + L::Z) + grp * kWave + lane;  // [group][lane]
+  uint32_t keep = 0;                         // dropout: this step's decisions (bit i = register i)
+  int h_cur = 0;                             // this step's query head (the dropout counter)
 
   // Phase 1: S (role P) or dP (role dS) for the group's 32 keys: A = Q / dO rows (row n,
   // chunk 2kc + g) of the staged tile, B = the group's K / V fragments.  Role P turns S
@@ -726,6 +367,29 @@ void bwd_kv_kernel(BwdArgs a) {
     for (int kc = 0; kc < KC; ++kc) {
       const V8 af = as_v8<V8>(ld_lds_16(src + n * L::ROWB + (((2 * kc + g) ^ kv_swz<D>(n)) * 16)));
       x = E::mfma(af, bf[kc], x);
+    }
+    if (DROP && !role_p) {
+      // Dropout decisions of the step for this lane's key, as bit i for query 8(i/4) +
+      // 4g + i%4.  The four lanes of a key quad (n = 4c .. 4c+3) share the Philox counter
+      // word key / 4: lane e = n % 4 makes the call of query 8j + 4g + e, and in round r
+      // it sends word (e + r) % 4 and receives, from quad lane (e - r) % 4, word e (its
+      // own key) of that lane's query.
+      const int e = n & 3;
+      uint32_t kb = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qt * kKVQ + 8 * j + 4 * g + e),
+                                       (uint32_t)(b * a.Hq + h_cur), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int wi = (e + r) & 3;
+          const uint32_t send = wi == 0 ? wv[0] : wi == 1 ? wv[1] : wi == 2 ? wv[2] : wv[3];
+          const uint32_t got = (uint32_t)__shfl((int)send, (lane & ~3) | ((e - r) & 3));
+          kb |= (got >= a.drop.thresh ? 1u : 0u) << (4 * j + ((e - r) & 3));
+        }
+      }
+      keep = kb;
+      zhand[0] = kb;
     }
     if (role_p) {
       // register i holds query 8(i/4) + 4g + i%4 of the step
@@ -756,6 +420,9 @@ void bwd_kv_kernel(BwdArgs a) {
     uint8_t* dsv = lds + L::DS + sb * L::DSS;
     uint8_t* dsr = dsv + L::DSS / 2;
     const uint8_t* src = lds + (role_p ? L::DO0 : L::Q0) + sb * L::QT;
+    if constexpr (DROP) {
+      if (role_p) keep = zhand[0];
+    }
     if (!role_p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -763,9 +430,14 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
-          x[i] = phand[i * kWave] * ((F8 ? dv_s * x[i] : x[i]) - dl[e]);
+          const float z = DROP ? (((keep >> i) & 1u) ? a.drop.rp : 0.f) : 1.f;
+          x[i] = phand[i * kWave] * (z * (F8 ? dv_s * x[i] : x[i]) - dl[e]);
         }
       }
+    } else if constexpr (DROP) {
+      // dV takes the kept probabilities, scaled by 1 / (1 - p)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] *= ((keep >> i) & 1u) ? a.drop.rp : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -857,6 +529,7 @@ void bwd_kv_kernel(BwdArgs a) {
     const bool work = step < nsteps;
     int h = 0, qt = 0;
     if (work) step_coords(step, h, qt);
+    h_cur = h;
     const int sb = step & 1;
     if (work) store_rows(sb);
     // this step's tiles have landed (own loads) and, after the barrier, everyone's;
@@ -1143,13 +816,21 @@ __global__ __launch_bounds__(kNT) void bwd_tree_kernel(BwdArgs a, int64_t n4) {
   for (int j = 0; j < 4; ++j) out[j] = (G)(v[0][j] * a.scale);
 }
 
-// column-owner launch for one (DQ, DROP) form
-template <typename T, typename G, int D, bool DQ, bool DROP>
-void main_k(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.causal)
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, true, DQ, DROP>), grid, dim3(kNTM), 0, stream, a);
-  else
-    hipLaunchKernelGGL((bwd_main_kernel<T, G, D, false, DQ, DROP>), grid, dim3(kNTM), 0, stream, a);
+// column-owner launch (16-bit operands) for one DQ form
+template <typename T, typename G, int D, bool DQ>
+void kv_k(const BwdArgs& a, dim3 gkv, hipStream_t stream) {
+  const dim3 blk(kKVW * kWave);
+  if (a.dropout) {
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, DQ, false, true>), gkv, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, DQ, false, true>), gkv, blk, 0, stream, a);
+  } else {
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, DQ>), gkv, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, DQ>), gkv, blk, 0, stream, a);
+  }
 }
 
 template <typename T, typename G, int D>
@@ -1159,7 +840,6 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kNT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((a.Sk + kBKV - 1) / kBKV), (unsigned)(a.B * a.Hkv));
   const int64_t n4 = rows * D / 4;
   const dim3 gkv((unsigned)((a.Sk + kKVT - 1) / kKVT), (unsigned)(a.B * a.Hkv));
   if constexpr (std::is_same<T, bf16>::value) {
@@ -1176,12 +856,7 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
     }
   }
   if (a.deterministic) {
-    if (a.dropout)
-      main_k<T, G, D, false, true>(a, grid, stream);
-    else if (a.causal)
-      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, false>), gkv, dim3(kKVW * kWave), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, false>), gkv, dim3(kKVW * kWave), 0, stream, a);
+    kv_k<T, G, D, false>(a, gkv, stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
@@ -1202,12 +877,7 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_tree_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
     return hipGetLastError();
   }
-  if (a.dropout)
-    main_k<T, G, D, true, true>(a, grid, stream);
-  else if (a.causal)
-    hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, true, true>), gkv, dim3(kKVW * kWave), 0, stream, a);
-  else
-    hipLaunchKernelGGL((bwd_kv_kernel<T, G, D, false, true>), gkv, dim3(kKVW * kWave), 0, stream, a);
+  kv_k<T, G, D, true>(a, gkv, stream);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_convert_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
