@@ -144,15 +144,19 @@ void fwd_kernel(FwdArgs a) {
   const int wg = blockIdx.x;
   // Workgroups go round-robin to the 8 XCDs (each with its own L2).  Padded layout:
   // the K/V head index (b, kvh) varies fastest, so the g query heads sharing a K/V head
-  // land on the same XCD whenever B Hkv is a multiple of 8.  Packed layout: the heads
-  // of one sequence stay adjacent (sequences differ in length; measured faster).
+  // land on the same XCD whenever B Hkv is a multiple of 8.  Packed layout: the heads of
+  // one sequence stay adjacent (sequences differ in length) and, among them, the K/V
+  // head varies fastest, so the g query heads of a K/V head are Hkv workgroups apart
+  // (one XCD when Hkv is a multiple of 8).
   const int bh = wg % BH;
   const int qt = CAUSAL ? (a.nqt - 1 - wg / BH) : (wg / BH);   // heavy causal tiles first
   int b, h, kvh;
   if constexpr (VL) {
     b = bh / a.Hq;
-    h = bh - b * a.Hq;
-    kvh = h / a.group;
+    const int hh = bh - b * a.Hq;
+    const int nkvh = a.Hq / a.group;
+    kvh = hh % nkvh;
+    h = kvh * a.group + hh / nkvh;
   } else {
     const int nkv = a.B * a.Hkv;
     const int bkv = bh % nkv;
