@@ -177,8 +177,8 @@ struct KvLds {
   static constexpr int DS = K + kKVT * ROWB;        // dS slots 0, 1: [128 keys][32 queries], 64-byte rows
   static constexpr int DSS = 2 * kKVT * kKVQ * 2;   // one slot: the values, then their bf16 residuals
   static constexpr int P = DS + 2 * DSS;            // P handoff [group][16 registers][64 lanes] float32
-  static constexpr int Z = P + kKG * 16 * kWave * 4; // dropout keep bits [group][64 lanes] uint32
-  static constexpr int BYTES = Z + kKG * kWave * 4;
+  static constexpr int Z = P + kKG * 16 * kWave * 4; // dropout keep bits [role][group][64 lanes] uint32
+  static constexpr int BYTES = Z + 2 * kKG * kWave * 4;
 };
 
 // Chunk swizzle of staged rows (Q, dO, K): chunk p of row r at position p ^ kv_swz(r).
@@ -352,7 +352,7 @@ void bwd_kv_kernel(BwdArgs a) {
     return tr_read(tile + r * L::ROWB + (((col >> 3) ^ kv_swz<D>(r)) * 16) + (col & 7) * 2);
   };
   float* phand = reinterpret_cast<float*>(lds + L::P) + grp * 16 * kWave + lane;   // [reg][lane]
-  uint32_t* zhand = reinterpret_cast<uint32_t*>(lds + L::Z) + grp * kWave + lane;  // [group][lane]
+  uint32_t* zhand = reinterpret_cast<uint32_t*>(lds + L::Z) + grp * kWave + lane;  // [role][group][lane]
   uint32_t keep = 0;                         // dropout: this step's decisions (bit i = register i)
   int h_cur = 0;                             // this step's query head (the dropout counter)
 
@@ -368,16 +368,18 @@ void bwd_kv_kernel(BwdArgs a) {
       const V8 af = as_v8<V8>(ld_lds_16(src + n * L::ROWB + (((2 * kc + g) ^ kv_swz<D>(n)) * 16)));
       x = E::mfma(af, bf[kc], x);
     }
-    if (DROP && !role_p) {
-      // Dropout decisions of the step for this lane's key, as bit i for query 8(i/4) +
-      // 4g + i%4.  The four lanes of a key quad (n = 4c .. 4c+3) share the Philox counter
-      // word key / 4: lane e = n % 4 makes the call of query 8j + 4g + e, and in round r
-      // it sends word (e + r) % 4 and receives, from quad lane (e - r) % 4, word e (its
-      // own key) of that lane's query.
+    // Dropout decisions of the step for this lane's key, as bit i for query 8(i/4) + 4g +
+    // i%4; draw(j0) makes query groups j0 and j0 + 1.  The four lanes of a key quad
+    // (n = 4c .. 4c+3) share the Philox counter word key / 4: lane e = n % 4 makes the call
+    // of query 8j + 4g + e, and in round r it sends word (e + r) % 4 and receives, from
+    // quad lane (e - r) % 4, word e (its own key) of that lane's query.  The roles split
+    // the draws: the dS wave makes groups 0, 1 after its dP product, the P wave groups 2, 3
+    // after its probabilities; each hands its half to the partner through LDS.
+    auto draw = [&](int j0) -> uint32_t {
       const int e = n & 3;
       uint32_t kb = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = j0; j < j0 + 2; ++j) {
         const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qt * kKVQ + 8 * j + 4 * g + e),
                                        (uint32_t)(b * a.Hq + h_cur), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
 #pragma unroll
@@ -388,8 +390,11 @@ void bwd_kv_kernel(BwdArgs a) {
           kb |= (got >= a.drop.thresh ? 1u : 0u) << (4 * j + ((e - r) & 3));
         }
       }
-      keep = kb;
-      zhand[0] = kb;
+      return kb;
+    };
+    if (DROP && !role_p) {
+      keep = draw(0);
+      zhand[0] = keep;
     }
     if (role_p) {
       // register i holds query 8(i/4) + 4g + i%4 of the step
@@ -409,6 +414,10 @@ void bwd_kv_kernel(BwdArgs a) {
           phand[i * kWave] = pv;
         }
       }
+      if constexpr (DROP) {
+        keep = draw(2);
+        zhand[kKG * kWave] = keep;
+      }
     }
   };
 
@@ -421,7 +430,7 @@ void bwd_kv_kernel(BwdArgs a) {
     uint8_t* dsr = dsv + L::DSS / 2;
     const uint8_t* src = lds + (role_p ? L::DO0 : L::Q0) + sb * L::QT;
     if constexpr (DROP) {
-      if (role_p) keep = zhand[0];
+      keep |= role_p ? zhand[0] : zhand[kKG * kWave];
     }
     if (!role_p) {
 #pragma unroll
