@@ -28,6 +28,32 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Deterministic-mode workspace: D rows | dq_splits float32 dQ partials (dq_splits > 1) |
+// per-block maxima and exponents | fp16 copies of q, dO, k, v (used for bf16 operands).
+// Returns the bytes needed; with a workspace, points a's fields into it.
+size_t det_layout(int B, int Hq, int Hkv, int Sq, int Sk, int d, int dq_splits, void* ws, bool bf16_ops,
+                  BwdArgs* a, BwdF16Ws* cw) {
+  const size_t rows = (size_t)B * Hq * Sq, krows = (size_t)B * Hkv * Sk;
+  const size_t o_part = align256(rows * sizeof(float));
+  const size_t o_amax = o_part + (dq_splits > 1 ? align256((size_t)dq_splits * rows * d * sizeof(float)) : 0);
+  const size_t o_q = o_amax + align256(kBwdAmaxBytes);
+  const size_t qbytes = align256(rows * d * 2), kbytes = align256(krows * d * 2);
+  const size_t o_do = o_q + qbytes, o_k = o_do + qbytes, o_v = o_k + kbytes;
+  if (a != nullptr) {
+    char* w = (char*)ws;
+    a->delta = (float*)w;
+    a->dq_part = dq_splits > 1 ? (float*)(w + o_part) : nullptr;
+    if (bf16_ops) {
+      cw->amax = (uint32_t*)(w + o_amax);
+      cw->copy[0] = w + o_q;
+      cw->copy[1] = w + o_k;
+      cw->copy[2] = w + o_v;
+      cw->copy[3] = w + o_do;
+    }
+  }
+  return o_v + kbytes;
+}
+
 int decode_chunks(int Smax, int chunk) { return (Smax + chunk - 1) / chunk; }
 
 }  // namespace
@@ -242,6 +268,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   const size_t rows = (size_t)B * Hq * Sq;
   BwdArgs a = {};
+  BwdF16Ws cw = {};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dO = dO;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dq_acc = (float*)workspace;
@@ -253,7 +280,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   a.grad_type = (int)grad_dtype;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+  return hip_status(attn_launch_bwd(a, &cw, (hipStream_t)stream));
 }
 
 int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
@@ -273,6 +300,7 @@ int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   const size_t rows = (size_t)B * Hq * Sq;
   BwdArgs a = {};
+  BwdF16Ws cw = {};
   a.q = q8; a.k = k8; a.v = v8; a.o = o; a.lse = lse; a.dO = dO;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dq_acc = (float*)workspace;
@@ -286,16 +314,14 @@ int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
   a.scale_log2 = scale * 1.4426950408889634f;
   a.fp8 = 1;
   a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
-  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+  return hip_status(attn_launch_bwd(a, &cw, (hipStream_t)stream));
 }
 
 size_t attn_bwd_deterministic_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                              int dq_splits) {
   if (check_dims(B, Hq, Hkv, Sq, Sk, d, false) != ATTN_OK) return 0;
   if (dq_splits < 1 || dq_splits > 16 || (dq_splits & (dq_splits - 1)) != 0) return 0;
-  const size_t rows = (size_t)B * Hq * Sq;
-  return align256(rows * sizeof(float)) +
-         (dq_splits > 1 ? align256((size_t)dq_splits * rows * d * sizeof(float)) : 0);
+  return det_layout(B, Hq, Hkv, Sq, Sk, d, dq_splits, nullptr, false, nullptr, nullptr);
 }
 
 int attn_bwd_deterministic(const void* q, const void* k, const void* v, const void* o,
@@ -316,13 +342,12 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
   if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;
   const size_t need = attn_bwd_deterministic_workspace_size(B, Hq, Hkv, Sq, Sk, d, dq_splits);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  const size_t rows = (size_t)B * Hq * Sq;
   BwdArgs a = {};
+  BwdF16Ws cw = {};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dO = dO;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dq_acc = nullptr;
-  a.delta = (float*)workspace;
-  a.dq_part = dq_splits > 1 ? (float*)((char*)workspace + align256(rows * sizeof(float))) : nullptr;
+  det_layout(B, Hq, Hkv, Sq, Sk, d, dq_splits, workspace, dtype == ATTN_BF16, &a, &cw);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Sq = Sq; a.Sk = Sk; a.d = d;
   a.group = Hq / Hkv;
   a.causal = causal != 0;
@@ -332,7 +357,7 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
   a.scale_log2 = scale * 1.4426950408889634f;
   a.deterministic = 1;
   a.dq_splits = dq_splits;
-  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+  return hip_status(attn_launch_bwd(a, &cw, (hipStream_t)stream));
 }
 
 int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -352,6 +377,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
   if (!isfinite(scale)) return ATTN_ERR_ARG;
   if ((int64_t)B * Hkv > 65535) return ATTN_ERR_SHAPE;
   BwdArgs a = {};
+  BwdF16Ws cw = {};
   if (!make_drop(dropout_p, seed, offset, &a.drop)) return ATTN_ERR_ARG;
   a.dropout = 1;
   const size_t rows = (size_t)B * Hq * Sq;
@@ -360,8 +386,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
     const size_t need = attn_bwd_deterministic_workspace_size(B, Hq, Hkv, Sq, Sk, d, dq_splits);
     if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     a.dq_acc = nullptr;
-    a.delta = (float*)workspace;
-    a.dq_part = dq_splits > 1 ? (float*)((char*)workspace + align256(rows * sizeof(float))) : nullptr;
+    det_layout(B, Hq, Hkv, Sq, Sk, d, dq_splits, workspace, dtype == ATTN_BF16, &a, &cw);
     a.deterministic = 1;
     a.dq_splits = dq_splits;
   } else {
@@ -379,7 +404,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
   a.grad_type = (int)grad_dtype;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(attn_launch_bwd(a, (hipStream_t)stream));
+  return hip_status(attn_launch_bwd(a, &cw, (hipStream_t)stream));
 }
 
 int attn_decode_pick_chunk(int B, int Hq, int Smax) {

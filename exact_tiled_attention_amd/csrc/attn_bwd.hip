@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kNT) void bwd_pre_kernel(BwdArgs a) {
   // sum over the LPR lanes of the row (LPR = 8 or 16 consecutive lanes)
 #pragma unroll
   for (int s = 1; s < LPR; s <<= 1) acc += __shfl_xor(acc, s);
-  if (row < rows && c8 == 0) a.delta[row] = acc;
+  // owners on fp16 copies of bf16 operands take D in the scale of dP (section 5)
+  if (row < rows && c8 == 0) a.delta[row] = a.f16_fac != nullptr ? acc * a.f16_fac[1] : acc;
 }
 
 // ---------------------------------------------------------------------------------
@@ -262,6 +263,9 @@ void bwd_kv_kernel(BwdArgs a) {
     dk_s = a.k_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
     dv_s = a.v_scale[(int64_t)(b * a.Hkv + kvh) * nkb + jt];
   }
+  // fp16 copies of bf16 operands: the score factor (section 5; D arrives in the scale of
+  // dP from the preprocess, the dK and dV factors are read at the end)
+  const float sl2b = a.f16_fac != nullptr ? a.f16_fac[0] : a.scale_log2;
   V8 bf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
@@ -556,7 +560,7 @@ void bwd_kv_kernel(BwdArgs a) {
     if (work) {
       const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
       const float dq_s = q_descale(h, qt);
-      const float sl2 = F8 ? a.scale_log2 * dq_s * dk_s : a.scale_log2;
+      const float sl2 = F8 ? a.scale_log2 * dq_s * dk_s : sl2b;
       f32x16 x;
       if (masked)
         phase1(std::true_type{}, qt, sb, sl2, x);
@@ -574,13 +578,17 @@ void bwd_kv_kernel(BwdArgs a) {
   // dV = sum P^T dO (role P), dK = scale sum dS^T Q (role dS); lane = d column 32db + n,
   // register i = key 8(i/4) + 4g + i%4 of the group's 32
   G* out = reinterpret_cast<G*>(role_p ? a.dv : a.dk) + ((int64_t)(b * a.Hkv + kvh) * a.Sk) * D;
-  const float f = role_p ? 1.f : a.scale;
+  float f = role_p ? 1.f : a.scale, f2 = 1.f;
+  if (a.f16_fac != nullptr) {
+    f = role_p ? a.f16_fac[2] : a.f16_fac[3];
+    f2 = role_p ? 1.f : a.f16_fac[4];
+  }
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = k0 + kKW * grp + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key < a.Sk) store_grad<G>(out + (int64_t)key * D + 32 * db + n, acc[db][i] * f);
+      if (key < a.Sk) store_grad<G>(out + (int64_t)key * D + 32 * db + n, acc[db][i] * f * f2);
     }
   }
 }
@@ -601,14 +609,16 @@ void bwd_kv_kernel(BwdArgs a) {
 //   P = exp2(S scale log2e - LSE log2e), dS = P (dP - D)   (per lane: one query)
 //   dQ^T += K^T dS^T (A = K^T by transpose reads of the K tile, B = dS^T in registers:
 //                     the accumulator layout of S^T is already the operand layout).
-// K and V tiles go straight to LDS (two-slot rings, loaded one tile ahead).
+// K and V tiles go straight to LDS (two-slot rings, loaded one tile ahead).  fp16
+// operands only: bf16 operands arrive as the exact fp16 copies of section 5.
 constexpr int kDqRW = 4;                   // waves (32 query rows each) per workgroup
 constexpr int kDqBQ = 32 * kDqRW;
 constexpr int kDqBC = 64;                  // keys per tile
 
-template <typename T, typename G, int D, bool CAUSAL, bool DROP>
+template <typename G, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kDqRW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(BwdArgs a) {
+  typedef f16 T;
   typedef Elem<T> E;
   typedef typename E::v8 V8;
   constexpr int BC = kDqBC;
@@ -672,6 +682,9 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   // rows past S_q: P = exp2(-inf) = 0, so they contribute nothing
   const float lse2 = qrow < a.Sq ? a.lse[rowq0 + qrow] * ATTN_LOG2E : INFINITY;
+  // fp16 copies of bf16 operands: the score factor (section 5; D arrives in the scale of
+  // dP from the preprocess, the dQ factors are read at the end)
+  const float sl2b = a.f16_fac != nullptr ? a.f16_fac[0] : a.scale_log2;
   const float dl = qrow < a.Sq ? a.delta[rowq0 + qrow] : 0.f;
   const int klim = CAUSAL ? min(a.Sk, qrow + (a.Sk - a.Sq) + 1) : a.Sk;
 
@@ -736,7 +749,7 @@ void bwd_dq_kernel(BwdArgs a) {
       // P and dS; register i is key t BC + 32 kbk + 8(i/4) + 4 grp + i%4
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(sc[i], a.scale_log2, -lse2));
+        float pv = fast_exp2(fmaf(sc[i], sl2b, -lse2));
         if constexpr (MASK) {
           const int key = t * BC + 32 * kbk + 8 * (i >> 2) + 4 * grp + (i & 3);
           pv = key < klim ? pv : 0.f;
@@ -749,10 +762,9 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int half = 0; half < 2; ++half) {
         const int cc = 2 * kbk + half;
         const int hb = half * 8;
-        // dS^T operand; bf16 also carries the residual dS - hi (a second product)
-        u32x4 dsp, dsl;
-        split_pack4x2<T>(f32x4{dp[hb + 0], dp[hb + 1], dp[hb + 2], dp[hb + 3]},
-                         f32x4{dp[hb + 4], dp[hb + 5], dp[hb + 6], dp[hb + 7]}, dsp, dsl);
+        // dS^T operand
+        const u32x4 dsp = {E::pack2(dp[hb + 0], dp[hb + 1]), E::pack2(dp[hb + 2], dp[hb + 3]),
+                           E::pack2(dp[hb + 4], dp[hb + 5]), E::pack2(dp[hb + 6], dp[hb + 7])};
         const int r0 = 16 * cc + 4 * grp + (s16 >> 2);
         const int r1 = r0 + 8;
 #pragma unroll
@@ -764,7 +776,6 @@ void bwd_dq_kernel(BwdArgs a) {
           const u32x2 hi = tr_read(ks + r1 * ROWB + ((ch ^ swz(r1)) * 16) + hf);
           const V8 kt8 = as_v8<V8>(u32x4{lo.x, lo.y, hi.x, hi.y});
           dq[db] = E::mfma(kt8, as_v8<V8>(dsp), dq[db]);
-          if constexpr (kSplit<T>) dq[db] = E::mfma(kt8, as_v8<V8>(dsl), dq[db]);
         }
         __builtin_amdgcn_sched_barrier(0);   // bound the transpose reads in flight
       }
@@ -784,6 +795,12 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 
   // dQ^T registers: lane column = query row, register i = d 32db + 8(i/4) + 4grp + i%4.
+  // fdq: the factor of a partial (the tree applies the scale) or of dQ itself
+  float fds = 1.f, fdq = a.dq_splits > 1 ? 1.f : a.scale;
+  if (a.f16_fac != nullptr) {
+    fds = a.f16_fac[3];
+    fdq = a.dq_splits > 1 ? a.f16_fac[6] : a.f16_fac[5];
+  }
   if (qrow < a.Sq) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -792,12 +809,12 @@ void bwd_dq_kernel(BwdArgs a) {
         const int dcol = 32 * db + 8 * r4 + 4 * grp;
         if (a.dq_splits > 1) {
           float* out = a.dq_part + ((int64_t)split * a.B * a.Hq * a.Sq + rowq0 + qrow) * D + dcol;
-          st_global_16(out, __builtin_bit_cast(u32x4, f32x4{dq[db][4 * r4], dq[db][4 * r4 + 1],
-                                                            dq[db][4 * r4 + 2], dq[db][4 * r4 + 3]}));
+          st_global_16(out, __builtin_bit_cast(u32x4, f32x4{dq[db][4 * r4] * fds * fdq, dq[db][4 * r4 + 1] * fds * fdq,
+                                                            dq[db][4 * r4 + 2] * fds * fdq, dq[db][4 * r4 + 3] * fds * fdq}));
         } else {
           G* out = reinterpret_cast<G*>(a.dq) + (rowq0 + qrow) * D + dcol;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) store_grad<G>(out + e, dq[db][4 * r4 + e] * a.scale);
+          for (int e = 0; e < 4; ++e) store_grad<G>(out + e, dq[db][4 * r4 + e] * fds * fdq);
         }
       }
   }
@@ -825,6 +842,116 @@ __global__ __launch_bounds__(kNT) void bwd_tree_kernel(BwdArgs a, int64_t n4) {
   for (int j = 0; j < 4; ++j) out[j] = (G)(v[0][j] * a.scale);
 }
 
+// ---------------------------------------------------------------------------------
+// 5. Deterministic mode with bf16 operands: exact fp16 copies.  A bf16 value has 8
+// significant bits, an fp16 value 11, so 2^k x of a bf16 x is an fp16 value whenever it
+// lies in fp16's normal range.  k is chosen per tensor so that its largest magnitude
+// lands in [4, 8) (for v, the larger of v's and o's, which bounds D).  Then |dP| and |D|
+// stay below d * 64 and |dS| = P |dP - D| below 2 d * 64 <= 16384, inside fp16's range,
+// and P and dS enter the dV, dK and dQ products as single fp16 operands (relative
+// rounding 2^-12) instead of bf16 hi + lo pairs.  Scaled values below 2^-14 become fp16
+// subnormals (absolute error at most 2^-25 in the scaled units).  The exponents are
+// clamped to [-60, 60] (largest magnitudes from 2^-58 to 2^63 are fully normalised), so
+// that every factor below is a float32: S carries 2^(eq+ek), dP and dS 2^(ed+ev) (D is
+// scaled to match), dV 2^ed, dK 2^(ed+ev+eq) and dQ 2^(ed+ev+ek); the owners multiply by
+//   [0] scale log2(e) 2^-(eq+ek)   [1] 2^(ed+ev) (D, in the preprocess)   [2] 2^-ed (dV)
+//   [3] 2^-(ed+ev), then [4] scale 2^-eq (dK) or [5] scale 2^-ek (dQ) or [6] 2^-ek (dQ
+//   partials; the tree applies the scale).  The powers of two are exact, so each result
+//   is rounded once.
+constexpr int kAmaxBlocks = kBwdAmaxBlocks;
+constexpr int kNumF16 = 4;                 // copies: q, k, v, dO
+
+// Largest magnitude of q, k, v, dO, o (blockIdx.y) over a grid-strided range of 16-byte
+// chunks, as bf16 bits without the sign (for values that are not NaN their order is the
+// order of the magnitudes; NaN sorts above infinity).
+__global__ __launch_bounds__(kNT) void bwd_amax_kernel(const void* q, const void* k, const void* v, const void* dO,
+                                                       const void* o, int64_t nq16, int64_t nk16, uint32_t* amax) {
+  const int t = blockIdx.y;
+  const u32x4* src = reinterpret_cast<const u32x4*>(t == 0 ? q : t == 1 ? k : t == 2 ? v : t == 3 ? dO : o);
+  const int64_t n16 = (t == 1 || t == 2) ? nk16 : nq16;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n16; i += (int64_t)kAmaxBlocks * kNT) {
+    const u32x4 x = ld_global_16(src + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(x[j] & 0x7FFFu, (x[j] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int st = 1; st < kWave; st <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, st));
+  __shared__ uint32_t wm[kNT / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) wm[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 1; i < kNT / kWave; ++i) m = max(m, wm[i]);
+    amax[t * kAmaxBlocks + blockIdx.x] = m;
+  }
+}
+
+// k with 2^k |x|max in [4, 8) from the bf16 bits of |x|max; 0 for zero, infinity, NaN
+__device__ inline int f16_exponent(uint32_t m) {
+  if (m == 0u || m >= 0x7F80u) return 0;
+  const int e = max((int)(m >> 7), 1);       // biased exponent (subnormals as 1)
+  return min(60, max(-60, 129 - e));
+}
+
+// One workgroup: reduce the per-block maxima, store the four exponents and the factors.
+__global__ __launch_bounds__(kNT) void bwd_f16_exp_kernel(uint32_t* amax, float scale, float scale_log2) {
+  const uint32_t* part = amax;
+  __shared__ uint32_t wm[5][kNT / kWave];
+#pragma unroll
+  for (int t = 0; t < 5; ++t) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < kAmaxBlocks; i += kNT) m = max(m, part[t * kAmaxBlocks + i]);
+#pragma unroll
+    for (int st = 1; st < kWave; st <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, st));
+    if ((threadIdx.x & (kWave - 1)) == 0) wm[t][threadIdx.x / kWave] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ex[kNumF16];
+#pragma unroll
+    for (int t = 0; t < kNumF16; ++t) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < kNT / kWave; ++i) {
+        m = max(m, wm[t][i]);
+        if (t == 2) m = max(m, wm[4][i]);    // v's exponent also covers o
+      }
+      ex[t] = f16_exponent(m);
+    }
+    int* eo = reinterpret_cast<int*>(amax + 5 * kAmaxBlocks);
+    float* fo = reinterpret_cast<float*>(eo + kNumF16);
+#pragma unroll
+    for (int t = 0; t < kNumF16; ++t) eo[t] = ex[t];
+    const int eq = ex[0], ek = ex[1], ev = ex[2], ed = ex[3];
+    fo[0] = ldexpf(scale_log2, -(eq + ek));
+    fo[1] = ldexpf(1.f, ed + ev);
+    fo[2] = ldexpf(1.f, -ed);
+    fo[3] = ldexpf(1.f, -(ed + ev));
+    fo[4] = ldexpf(scale, -eq);
+    fo[5] = ldexpf(scale, -ek);
+    fo[6] = ldexpf(1.f, -ek);
+  }
+}
+
+// fp16 copy 2^k x of q, k, v, dO (blockIdx.y), 8 values per thread and iteration.
+__global__ __launch_bounds__(kNT) void bwd_to_f16_kernel(const void* q, const void* k, const void* v, const void* dO,
+                                                         BwdF16Ws ws, int64_t nq16, int64_t nk16) {
+  const int t = blockIdx.y;
+  const int e = reinterpret_cast<const int*>(ws.amax + 5 * kAmaxBlocks)[t];
+  const u32x4* src = reinterpret_cast<const u32x4*>(t == 0 ? q : t == 1 ? k : t == 2 ? v : dO);
+  u32x4* dst = reinterpret_cast<u32x4*>(ws.copy[t]);
+  const int64_t n16 = (t == 1 || t == 2) ? nk16 : nq16;
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n16; i += (int64_t)gridDim.x * kNT) {
+    const u32x4 x = ld_global_16(src + i);
+    u32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      y[j] = Elem<f16>::pack2(ldexpf(__uint_as_float(x[j] << 16), e), ldexpf(__uint_as_float(x[j] & 0xFFFF0000u), e));
+    st_global_16(dst + i, y);
+  }
+}
+
 // column-owner launch (16-bit operands) for one DQ form
 template <typename T, typename G, int D, bool DQ>
 void kv_k(const BwdArgs& a, dim3 gkv, hipStream_t stream) {
@@ -842,13 +969,46 @@ void kv_k(const BwdArgs& a, dim3 gkv, hipStream_t stream) {
   }
 }
 
-template <typename T, typename G, int D>
-hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  constexpr int RPB = kNT / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kNT), 0, stream, a);
+// deterministic mode after the preprocess, on fp16 operands: column owner without dQ,
+// query-row owner, and the partials' tree when dq_splits > 1
+template <typename G, int D>
+hipError_t launch_det(const BwdArgs& a, dim3 gkv, int64_t n4, hipStream_t stream) {
+  kv_k<f16, G, D, false>(a, gkv, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
+  const dim3 gq((unsigned)(nqt * a.B * a.Hq), (unsigned)a.dq_splits);
+  if (a.dropout) {
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<G, D, true, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<G, D, false, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
+  } else {
+    if (a.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<G, D, true, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<G, D, false, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess || a.dq_splits == 1) return e;
+  hipLaunchKernelGGL((bwd_tree_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
+  return hipGetLastError();
+}
+
+template <typename T, typename G, int D>
+hipError_t launch_bwd_tg(const BwdArgs& a, const BwdF16Ws* cw, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  constexpr int RPB = kNT / (D / 8);
+  auto pre = [&](const BwdArgs& x) {
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kNT), 0, stream, x);
+    return hipGetLastError();
+  };
+  hipError_t e = hipSuccess;
+  const bool copies = std::is_same<T, bf16>::value && a.deterministic;
+  if (!copies) {
+    e = pre(a);
+    if (e != hipSuccess) return e;
+  }
   const int64_t n4 = rows * D / 4;
   const dim3 gkv((unsigned)((a.Sk + kKVT - 1) / kKVT), (unsigned)(a.B * a.Hkv));
   if constexpr (std::is_same<T, bf16>::value) {
@@ -865,26 +1025,31 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
     }
   }
   if (a.deterministic) {
-    kv_k<T, G, D, false>(a, gkv, stream);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nqt = (a.Sq + kDqBQ - 1) / kDqBQ;
-    const dim3 gq((unsigned)(nqt * a.B * a.Hq), (unsigned)a.dq_splits);
-    if (a.dropout) {
-      if (a.causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, true, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, false, true>), gq, dim3(kDqRW * kWave), 0, stream, a);
+    if constexpr (std::is_same<T, bf16>::value) {
+      // exact fp16 copies of q, k, v, dO, then the fp16 owners on them
+      if (cw == nullptr || cw->amax == nullptr) return hipErrorInvalidValue;
+      const int64_t nq16 = rows * D / 8, nk16 = (int64_t)a.B * a.Hkv * a.Sk * D / 8;
+      hipLaunchKernelGGL(bwd_amax_kernel, dim3(kAmaxBlocks, 5), dim3(kNT), 0, stream, a.q, a.k, a.v, a.dO, a.o,
+                         nq16, nk16, cw->amax);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_f16_exp_kernel, dim3(1), dim3(kNT), 0, stream, cw->amax, a.scale, a.scale_log2);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_to_f16_kernel, dim3(1024, kNumF16), dim3(kNT), 0, stream, a.q, a.k, a.v, a.dO, *cw,
+                         nq16, nk16);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      BwdArgs c = a;
+      c.f16_fac = reinterpret_cast<const float*>(cw->amax + 5 * kAmaxBlocks + kNumF16);
+      e = pre(c);                        // D from the bf16 o and dO, in the scale of dP
+      if (e != hipSuccess) return e;
+      c.q = cw->copy[0]; c.k = cw->copy[1]; c.v = cw->copy[2]; c.dO = cw->copy[3];
+      c.dtype_bf16 = 0;
+      return launch_det<G, D>(c, gkv, n4, stream);
     } else {
-      if (a.causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, true, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
-      else
-        hipLaunchKernelGGL((bwd_dq_kernel<T, G, D, false, false>), gq, dim3(kDqRW * kWave), 0, stream, a);
+      return launch_det<G, D>(a, gkv, n4, stream);
     }
-    e = hipGetLastError();
-    if (e != hipSuccess || a.dq_splits == 1) return e;
-    hipLaunchKernelGGL((bwd_tree_kernel<G>), dim3((unsigned)((n4 + kNT - 1) / kNT)), dim3(kNT), 0, stream, a, n4);
-    return hipGetLastError();
   }
   kv_k<T, G, D, true>(a, gkv, stream);
   e = hipGetLastError();
@@ -894,21 +1059,21 @@ hipError_t launch_bwd_tg(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <typename T, typename G>
-hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 64) return launch_bwd_tg<T, G, 64>(a, stream);
-  return launch_bwd_tg<T, G, 128>(a, stream);
+hipError_t launch_bwd_d(const BwdArgs& a, const BwdF16Ws* cw, hipStream_t stream) {
+  if (a.d == 64) return launch_bwd_tg<T, G, 64>(a, cw, stream);
+  return launch_bwd_tg<T, G, 128>(a, cw, stream);
 }
 
 template <typename T>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  if (a.grad_type == ATTN_F32) return launch_bwd_d<T, float>(a, stream);
-  if (a.grad_type == ATTN_BF16) return launch_bwd_d<T, bf16>(a, stream);
-  return launch_bwd_d<T, f16>(a, stream);
+hipError_t launch_bwd_t(const BwdArgs& a, const BwdF16Ws* cw, hipStream_t stream) {
+  if (a.grad_type == ATTN_F32) return launch_bwd_d<T, float>(a, cw, stream);
+  if (a.grad_type == ATTN_BF16) return launch_bwd_d<T, bf16>(a, cw, stream);
+  return launch_bwd_d<T, f16>(a, cw, stream);
 }
 
 }  // namespace
 
-hipError_t attn_launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  if (a.dtype_bf16) return launch_bwd_t<bf16>(a, stream);
-  return launch_bwd_t<f16>(a, stream);
+hipError_t attn_launch_bwd(const BwdArgs& a, const BwdF16Ws* cw, hipStream_t stream) {
+  if (a.dtype_bf16) return launch_bwd_t<bf16>(a, cw, stream);
+  return launch_bwd_t<f16>(a, cw, stream);
 }

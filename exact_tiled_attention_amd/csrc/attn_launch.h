@@ -81,7 +81,23 @@ struct BwdArgs {
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
+  // owners running on exact fp16 copies of bf16 operands: the factors that undo the
+  // copies' powers of two (section 5 of the backward); null otherwise
+  const float* f16_fac;
 };
+
+// Deterministic mode with bf16 operands: workspace of the exact fp16 copies (host side,
+// read by the preparation kernels only).  amax: [5][kBwdAmaxBlocks] per-block maxima of
+// q, k, v, dO, o, then the 4 exponents (int) and kBwdFacs factors (float); copy: the
+// fp16 copies of q, k, v, dO.
+struct BwdF16Ws {
+  uint32_t* amax;
+  void* copy[4];
+};
+constexpr int kBwdAmaxBlocks = 512;
+constexpr int kBwdFacs = 7;
+// bytes of BwdF16Ws::amax (maxima, exponents, factors)
+constexpr size_t kBwdAmaxBytes = (5 * kBwdAmaxBlocks + 4 + kBwdFacs) * sizeof(uint32_t);
 
 struct DecodeArgs {
   const void* q;
@@ -117,7 +133,7 @@ hipError_t attn_launch_exp2_soft(const float* x, float* y, int64_t n, hipStream_
 hipError_t attn_launch_fp8_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t attn_launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 int attn_fp8_tile_keys();
-hipError_t attn_launch_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t attn_launch_bwd(const BwdArgs& a, const BwdF16Ws* f16, hipStream_t stream);
 hipError_t attn_launch_decode(const DecodeArgs& a, hipStream_t stream);
 // device address of the current GPU's decode scratch (ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
 hipError_t attn_decode_scratch(void** ptr);

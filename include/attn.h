@@ -262,10 +262,19 @@ int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_
  * tiles are cut into that many contiguous ranges, each writes a float32 partial, and
  * the partials are summed in a fixed binary tree.  The recomputation costs two more
  * matrix products per tile than attn_bwd's atomic dQ.
+ * bf16 operands: q, k, v and dO are first copied into the workspace as fp16 values
+ * scaled by one power of two per tensor, chosen from the tensor's largest magnitude (and
+ * o's, for v) so that it lands in [4, 8); a bf16 value scaled so is an fp16 value unless
+ * it falls below fp16's normal range (2^-14 after scaling), so the copies are exact
+ * there.  Both owners then run on the copies with fp16 products: P and dS enter dV, dK
+ * and dQ as single fp16 operands (relative rounding 2^-12) where attn_bwd uses bf16 hi +
+ * lo pairs, and the scales are undone in float32 at the end.  The exponents are clamped
+ * to [-60, 60].
  *
  *   Arguments as attn_bwd, plus dq_splits (1, 2, 4, 8 or 16; else ATTN_ERR_ARG).
  *   workspace: >= attn_bwd_deterministic_workspace_size(..., dq_splits) bytes
- *       (D rows, and the dq_splits partials when dq_splits > 1)             (scratch)
+ *       (D rows, the dq_splits partials when dq_splits > 1, the fp16 copies of q, dO,
+ *       k, v and their exponents; the size does not depend on the dtype)    (scratch)
  */
 size_t attn_bwd_deterministic_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d,
                                              int dq_splits);

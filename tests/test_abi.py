@@ -185,6 +185,8 @@ def test_bwd_deterministic_argument_checks():
     ws1 = lib.attn_bwd_deterministic_workspace_size(1, 4, 2, 8, 8, 64, 1)
     ws4 = lib.attn_bwd_deterministic_workspace_size(1, 4, 2, 8, 8, 64, 4)
     assert ws1 >= 1 * 4 * 8 * 4 and ws4 >= ws1 + 4 * 1 * 4 * 8 * 64 * 4
+    # room for the fp16 copies of q, dO (4 x 8 rows) and k, v (2 x 8 rows) of bf16 operands
+    assert ws1 >= 1 * 4 * 8 * 4 + 2 * (4 * 8 * 64 * 2) + 2 * (2 * 8 * 64 * 2)
     assert lib.attn_bwd_deterministic_workspace_size(1, 4, 2, 8, 8, 64, 3) == 0
     def call(splits=1, ws_bytes=ws1, **kw):
         a = dict(B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=64)

@@ -82,3 +82,50 @@ def test_deterministic_16bit_gradients():
     f32 = _grads(w, grad_dtype=torch.float32)
     for x, y in zip(got, f32):
         assert torch.equal(x, y.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("dq_splits", [1, 4])
+def test_deterministic_bf16_power_of_two_inputs(dq_splits):
+    """bf16 operands run on fp16 copies scaled by one power of two per tensor.  Inputs
+    scaled as q 2^10, k 2^-10 (S unchanged), v 2^20 and dO 2^-30 give the same copies, so
+    the gradients are the unscaled ones times 2^-20 (dQ), 1 (dK) and 2^-30 (dV), bit for
+    bit: a wrong exponent, a factor applied twice or a lost one shows here."""
+    need_gpu()
+    import exact_tiled_attention_amd as eta
+    w = attn_inputs.prefill(1, 8, 2, 333, 517, 128, "bf16", seed=75, causal=True, with_grad=True)
+    t, p = w.tensors, w.params
+    q, k, v, do = (to_dev(t[n]) for n in ("q", "k", "v", "do"))
+
+    def grads(q, k, v, do):
+        o, lse = eta.attn_fwd(q, k, v, scale=p["scale"], causal=True)
+        g = eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=True, grad_dtype=torch.float32,
+                         deterministic=True, dq_splits=dq_splits)
+        torch.cuda.synchronize()
+        return [x.cpu() for x in g]
+
+    say(f"[bwd-det] power-of-two scaled bf16 inputs, splits={dq_splits}")
+    base = grads(q, k, v, do)
+    scaled = grads(q * 2.0 ** 10, k * 2.0 ** -10, v * 2.0 ** 20, do * 2.0 ** -30)
+    assert torch.equal(scaled[0] * 2.0 ** 20, base[0])
+    assert torch.equal(scaled[1], base[1])
+    assert torch.equal(scaled[2] * 2.0 ** 30, base[2])
+    ref = dense.backward(t["q"], t["k"], t["v"], t["do"], p["scale"], True, o_storage=t["q"].dtype)[:3]
+    for n, g_, r_ in zip(("dq", "dk", "dv"), base, ref):
+        assert_close_out(g_, r_, TOL_GRAD, f"power-of-two base {n}")
+
+
+def test_deterministic_bf16_small_gradients():
+    """dO of magnitude 2^-40 (a loss averaged over many tokens): the copies carry it at
+    full fp16 precision, so the gradients keep their relative accuracy."""
+    need_gpu()
+    import exact_tiled_attention_amd as eta
+    w = attn_inputs.prefill(1, 4, 2, 200, 300, 64, "bf16", seed=76, causal=False, with_grad=True)
+    t, p = w.tensors, w.params
+    q, k, v, do = (to_dev(t[n]) for n in ("q", "k", "v", "do"))
+    o, lse = eta.attn_fwd(q, k, v, scale=p["scale"], causal=False)
+    g = eta.attn_bwd(q, k, v, o, lse, do * 2.0 ** -40, scale=p["scale"], causal=False, grad_dtype=torch.float32,
+                     deterministic=True)
+    torch.cuda.synchronize()
+    ref = dense.backward(t["q"], t["k"], t["v"], t["do"], p["scale"], False, o_storage=t["q"].dtype)[:3]
+    for n, g_, r_ in zip(("dq", "dk", "dv"), g, ref):
+        assert_close_out(g_.cpu() * 2.0 ** 40, r_, TOL_GRAD, f"dO 2^-40 {n}")
