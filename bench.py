@@ -143,7 +143,7 @@ def bench_fwd(name, w, steps, warmup, torch, eta, dropout_p=None, exp_emulated=N
             "peak": PEAK_TFLOPS[p["dtype"]]}, (q, k, v, o, lse)
 
 
-def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False, dropout_p=None):
+def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False, dropout_p=None, atomic=False):
     t, p = w.tensors, w.params
     q, k, v, o, lse = fwd_bufs
     do = t["do"].cuda()
@@ -158,11 +158,13 @@ def bench_bwd(name, w, fwd_bufs, steps, warmup, torch, eta, deterministic=False,
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
     fn = lambda: eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"],
                               grad_dtype=torch.float32, workspace=ws, dq=dq, dk=dk, dv=dv,
-                              deterministic=deterministic, dropout_p=dropout_p, seed=1234, offset=0)
+                              deterministic=deterministic, dropout_p=dropout_p, seed=1234, offset=0,
+                              atomic=atomic)
     t_ = _time_launches(fn, steps, warmup, torch)
     flops = 2.5 * _fwd_flops(p["B"], p["Hq"], p["Sq"], p["Sk"], p["d"], p["causal"])
-    kern = ("bwd deterministic (preprocess + column owner dK/dV + query owner dQ)" if deterministic
-            else "bwd (preprocess + main + convert)")
+    split = deterministic or (not atomic and p["Sk"] >= 1024)
+    kern = ("bwd with the query-row owner's dQ (preprocess + column owner dK/dV + query owner dQ)" if split
+            else "bwd with atomic dQ (preprocess + column owner + convert)")
     return {"workload": name, "kernel": kern, **_timing_fields(t_),
             "tflops": flops / (t_["ms_mean"] * 1e-3) / 1e12, "flops_per_call": flops, "dtype": p["dtype"],
             "peak": PEAK_TFLOPS[p["dtype"]]}
@@ -293,6 +295,8 @@ def run_extra(want, steps, warmup, torch, eta, attn_inputs):
         r, bufs = bench_fwd(name + " fwd", w3, n, warmup, torch, eta)
         configs["causal_gqa_fwd"] = r
         _guard(configs, "causal_gqa_bwd", lambda: bench_bwd(name + " bwd", w3, bufs, n, warmup, torch, eta), eta)
+        _guard(configs, "causal_gqa_bwd_atomic",
+               lambda: bench_bwd(name + " bwd, atomic dQ form", w3, bufs, n, warmup, torch, eta, atomic=True), eta)
         _guard(configs, "causal_gqa_bwd_deterministic",
                lambda: bench_bwd(name + " bwd, deterministic", w3, bufs, n, warmup, torch, eta,
                                  deterministic=True), eta)

@@ -261,11 +261,16 @@ def bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d) -> int:
 
 def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.float32,
              workspace=None, dq=None, dk=None, dv=None, stream=None, deterministic=False, dq_splits=1,
-             dropout_p=None, seed=0, offset=0):
+             dropout_p=None, seed=0, offset=0, atomic=False):
     """dQ, dK, dV of attn_fwd (dK/dV already summed over each K/V head's query group).
-    deterministic=True: no atomics, bitwise-repeatable results; dQ from a query-row owner
-    over dq_splits (1, 2, 4, 8, 16) key ranges whose partials are summed in a fixed tree.
-    dropout_p (with seed, offset): the backward of attn_fwd_dropout with the same values."""
+    Default: dQ in the library's form for the key length (atomic adds below 1024 keys,
+    the query-row owner from there on).  atomic=True: the column owner's atomic dQ at
+    every length.  deterministic=True: no atomics, bitwise-repeatable results; dQ from a
+    query-row owner over dq_splits (1, 2, 4, 8, 16) key ranges whose partials are summed
+    in a fixed tree.  dropout_p (with seed, offset): the backward of attn_fwd_dropout with
+    the same values."""
+    if atomic and (deterministic or dropout_p is not None):
+        raise ValueError("atomic=True excludes deterministic and dropout_p")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _require(t, n, 4)
     B, Hq, Sq, d = q.shape
@@ -303,10 +308,11 @@ def attn_bwd(q, k, v, o, lse, do, scale=None, causal=False, grad_dtype=torch.flo
                                           ws_bytes, _stream(stream))
         _lib.check("attn_bwd_deterministic", st)
     else:
-        st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                            _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), _code(q.dtype),
-                            _code(grad_dtype), _ptr(workspace), ws_bytes, _stream(stream))
-        _lib.check("attn_bwd", st)
+        name = "attn_bwd_atomic" if atomic else "attn_bwd"
+        st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), B, Hq, Hkv, Sq, Sk, d, scale, int(bool(causal)), _code(q.dtype),
+                                  _code(grad_dtype), _ptr(workspace), ws_bytes, _stream(stream))
+        _lib.check(name, st)
     return dq, dk, dv
 
 

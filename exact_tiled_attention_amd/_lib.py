@@ -32,6 +32,7 @@ PROTOTYPES = {
     "attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S, _P]),
+    "attn_bwd_atomic": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P, _S, _P]),
     "attn_fp8_quantize": (_I, [_P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P]),
     "attn_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _I, _P]),
     "attn_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _F, _U64, _U32,

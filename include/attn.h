@@ -203,17 +203,23 @@ int attn_fp8_kv_tile(void);
  * each workgroup owns one K/V column tile of one K/V head, recomputes
  * P = exp(scale Q K^T - LSE) tile by tile for every query head of the group,
  * forms dS = P * (dP - D), keeps dK/dV in registers (the group sum over the query
- * heads sharing the K/V head is done in the owner, section 0x06E) and adds
- * dQ contributions to a float32 accumulator with atomics (section 0x06.1F);
- * a last pass scales and converts dQ.
+ * heads sharing the K/V head is done in the owner, section 0x06E).  dQ has two forms
+ * (section 0x06.1F and the ownership table of section 0x06.1G), chosen by key length:
+ *   Sk < 1024: the column owner adds its dQ contributions to a float32 accumulator
+ *       with atomics and a last pass scales and converts dQ (attn_bwd_atomic);
+ *   Sk >= 1024: a query-row owner recomputes P and dS and writes dQ directly, exactly
+ *       as attn_bwd_deterministic with dq_splits = 1 (each 128-key column tile's
+ *       atomic adds are one float32 pass over the dQ accumulator, performed past the
+ *       L2; from about 1024 keys on they cost more than the recomputation).
  *
  *   q,o,dO [B,Hq,Sq,d] and k,v [B,Hkv,Sk,d]: element type `dtype`              (in)
  *   lse [B,Hq,Sq] float32 as written by attn_fwd                              (in)
  *   dq [B,Hq,Sq,d], dk/dv [B,Hkv,Sk,d]: element type `grad_dtype`
  *       (ATTN_F32, ATTN_BF16 or ATTN_F16)                                      (out)
  *   workspace: >= attn_bwd_workspace_size(...) bytes of device memory, any
- *       content on entry (float32 dQ accumulator + D rows)                   (scratch)
- *   Requires Sk >= 1.  Results of the atomic dQ sum are not bitwise repeatable.
+ *       content on entry (enough for either form: the float32 dQ accumulator and D
+ *       rows, or the deterministic form's D rows and fp16 copies)            (scratch)
+ *   Requires Sk >= 1.  Results of the atomic form are not bitwise repeatable.
  */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -221,6 +227,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
              attn_dtype_t dtype, attn_dtype_t grad_dtype,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd_atomic -- attn_bwd with the column owner's atomic dQ at every key length
+ * ("M4.4 - FlashAttention-2 ...", section 0x06.1, Algorithm 2 and section 0x06.1F).
+ * Arguments and workspace as attn_bwd.
+ */
+int attn_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                    attn_dtype_t dtype, attn_dtype_t grad_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_bwd_fp8 -- backward of attention on E4M3 operands with per-block descales: the
@@ -292,8 +309,8 @@ int attn_bwd_deterministic(const void* q, const void* k, const void* v, const vo
  * dV = (P Z)^T dO, dS = P (Z dP - D), dQ = scale dS K, dK = scale dS^T Q.
  *
  *   Arguments as attn_bwd, plus dropout_p, seed, offset as given to attn_fwd_dropout,
- *   deterministic (0: atomic dQ as attn_bwd, workspace attn_bwd_workspace_size;
- *   1: as attn_bwd_deterministic with dq_splits, workspace
+ *   deterministic (0: dQ in attn_bwd's form for the key length, workspace
+ *   attn_bwd_workspace_size; 1: as attn_bwd_deterministic with dq_splits, workspace
  *   attn_bwd_deterministic_workspace_size).
  */
 int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -103,6 +103,13 @@ def test_bwd_and_workspace_checks():
     assert call(grad=3) == -5 and call(dtype=2) == -5
     assert call(Sk=0) == -2 and call(Hkv=3) == -3 and call(d=32) == -4
     assert lib.attn_bwd(None, P, P, P, P, P, P, P, P, 1, 4, 2, 8, 8, 64, 0.125, 0, 1, 2, P, ws, None) == -1
+    # the atomic form takes the same arguments and workspace
+    assert lib.attn_bwd_atomic(P, P, P, P, P, P, P, P, P, 1, 4, 2, 8, 8, 64, 0.125, 1, 1, 2, None, ws, None) == -6
+    assert lib.attn_bwd_atomic(P, P, P, P, P, P, P, P, P, 1, 4, 3, 8, 8, 64, 0.125, 1, 1, 2, P, ws, None) == -3
+    # enough for either form: at 1024 keys and more attn_bwd runs the deterministic form
+    for sk in (8, 1024):
+        assert lib.attn_bwd_workspace_size(1, 4, 2, 8, sk, 64) >= lib.attn_bwd_deterministic_workspace_size(
+            1, 4, 2, 8, sk, 64, 1)
 
 
 def test_decode_and_fp8_checks():

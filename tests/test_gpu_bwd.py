@@ -1,4 +1,5 @@
-"""GPU parity of attn_bwd (from the GPU forward's O and LSE) against the float64 oracle."""
+"""GPU parity of attn_bwd and attn_bwd_atomic (from the GPU forward's O and LSE) against
+the float64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -10,20 +11,21 @@ from gpu_common import TOL_GRAD, assert_close_out, need_gpu, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_grads(w, grad_dtype=torch.float32):
+def _gpu_grads(w, grad_dtype=torch.float32, atomic=False, deterministic=False):
     import exact_tiled_attention_amd as eta
     t, p = w.tensors, w.params
     q, k, v, do = (to_dev(t[n]) for n in ("q", "k", "v", "do"))
     o, lse = eta.attn_fwd(q, k, v, scale=p["scale"], causal=p["causal"])
-    dq, dk, dv = eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"], grad_dtype=grad_dtype)
+    dq, dk, dv = eta.attn_bwd(q, k, v, o, lse, do, scale=p["scale"], causal=p["causal"], grad_dtype=grad_dtype,
+                              atomic=atomic, deterministic=deterministic)
     torch.cuda.synchronize()
     return dq, dk, dv
 
 
-def _check(w, grad_dtype=torch.float32, heads=None):
+def _check(w, grad_dtype=torch.float32, heads=None, atomic=False):
     t, p = w.tensors, w.params
-    say(f"[bwd] {w.name} causal={p['causal']} grad={grad_dtype}")
-    dq, dk, dv = _gpu_grads(w, grad_dtype)
+    say(f"[bwd] {w.name} causal={p['causal']} grad={grad_dtype} atomic={atomic}")
+    dq, dk, dv = _gpu_grads(w, grad_dtype, atomic=atomic)
     # D is formed from the forward output as stored in the element type
     dQ, dK, dV, _ = dense.backward(t["q"], t["k"], t["v"], t["do"], p["scale"], p["causal"], heads=heads,
                                    o_storage=t["q"].dtype)
@@ -82,7 +84,27 @@ def test_bwd_atomic_dq_repeat_within_tolerance():
     assert (a[0] - b[0]).abs().max().item() <= 1e-5                    # dQ: unordered float adds
 
 
-def test_bwd_causal_gqa_full_size_one_kv_head():
+@pytest.mark.parametrize("atomic", [False, True])
+def test_bwd_causal_gqa_full_size_one_kv_head(atomic):
     need_gpu()
     w = attn_inputs.CONFIGS["causal_gqa_bf16_2x32x8192_kv8_d128"]()
-    _check(w, heads=[(1, 5)])
+    _check(w, heads=[(1, 5)], atomic=atomic)
+
+
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("f16", False)])
+def test_bwd_atomic_form_long_keys(dtype, causal):
+    """attn_bwd_atomic keeps the column owner's atomic dQ where attn_bwd switches form."""
+    need_gpu()
+    w = attn_inputs.prefill(1, 8, 2, 700, 1100, 128, dtype, seed=42, causal=causal, with_grad=True)
+    _check(w, atomic=True)
+
+
+def test_bwd_long_keys_take_the_query_row_owner():
+    """From 1024 keys on, attn_bwd is the deterministic form with one key range."""
+    need_gpu()
+    w = attn_inputs.prefill(1, 8, 2, 700, 1100, 128, "bf16", seed=43, causal=True, with_grad=True)
+    _check(w)
+    a = _gpu_grads(w)
+    b = _gpu_grads(w, deterministic=True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
