@@ -23,9 +23,13 @@
 // kept in units of the current tile's V descale s_v, and moving to a tile with
 // descale dV_j multiplies it by alpha * s_v / dV_j.
 //
-// V^T is stored in LDS with the keys of each d row permuted so that the 32 keys a lane
-// group needs for one 64-key contraction are 32 contiguous bytes: key k lives at byte
-// 32 * ((k >> 2) & 1) + ((k >> 3) << 2) + (k & 3) of its row.
+// V goes from HBM straight into LDS (buffer loads with the LDS destination), row-major
+// with its rows permuted and its 16-byte chunks swizzled; the V^T operand of the P V
+// product comes from ds_read_b64_tr_b8, which hands each lane of a 16-lane group one
+// byte column (one d) of 8 rows.  Slot j of lane group g of a 64-key contraction is key
+// 8 (j / 4) + 4 g + j % 4 (the keys the S^T accumulator put in that lane's registers), so
+// LDS row r holds key r with bits 2 and 3 exchanged: the 8 slots 8m .. 8m+7 of group g
+// are then the 8 consecutive rows 16m + 8g .. +7.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -37,17 +41,31 @@ namespace {
 constexpr int kWave = 64;
 constexpr int BC = 64;
 constexpr int SCALE_ROWS = 128;
+constexpr int kStages = 3;      // LDS stages of the K/V tile ring
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 template <int D>
 struct Fp8Lds {
   static constexpr int KSTR = D + 8;      // bf16 elements per K row (widened from E4M3)
-  static constexpr int VSTR = BC + 16;    // bytes per V^T row (E4M3)
   static constexpr int K_BYTES = BC * KSTR * 2;
-  static constexpr int V_BYTES = D * VSTR;
+  static constexpr int V_BYTES = BC * D;  // E4M3 rows, permuted and swizzled
   static constexpr int STAGE = K_BYTES + V_BYTES;
 };
+
+// LDS row r of a V tile holds key r with bits 2 and 3 exchanged.
+__device__ inline int v_row_key(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+// Chunk p of LDS V row r holds the row's 16-byte chunk p ^ v_swz(r): the 8 rows a
+// transpose read takes then fall on distinct banks.
+template <int D> __device__ inline int v_swz(int r) { return D == 128 ? (r & 7) : ((r >> 2) & 1); }
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+// ds_read_b64_tr_b8: in each 16-lane group, lanes 2k and 2k+1 address the two 8-byte
+// halves of row k of an 8 x 16-byte block; lane i receives byte i of rows 0 .. 7.
+__device__ inline u32x2 tr8_read(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p));
+}
 
 __device__ inline f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // format 0 (E4M3) for both operands, block scales fixed at 2^0 (E8M0 code 127)
@@ -73,8 +91,6 @@ __device__ inline float max_pair32(float x) {
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ inline int vt_pos(int k) { return 32 * ((k >> 2) & 1) + ((k >> 3) << 2) + (k & 3); }
-
 template <int D, int NW, bool OF32>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void fp8_fwd_kernel(Fp8Args a) {
   // causal masking is a runtime flag: the plans and the per-lane key limit below carry it
@@ -83,9 +99,10 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int NT = NW * kWave;
   constexpr int BQ = NW * 32;
   constexpr int K_LOADS = (BC * D / 16 + NT - 1) / NT;     // 16-byte K chunks per thread
-  constexpr int V_BLOCKS = (BC / 4) * (D / 16);            // 4-key x 16-d byte blocks
+  constexpr int CPR = D / 16;                              // 16-byte chunks per V row
+  constexpr int V_LOADS = (BC * CPR + NT - 1) / NT;        // direct V loads per thread
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * L::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,9 +162,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   float s_v = 1.f;   // V descale the accumulator is expressed in
 
   u32x4 kreg[K_LOADS];
-  u32x4 vreg[4];
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, (uint32_t)a.Sk * D);   // keys past S_k read 0
 
-  auto load_tile = [&](int t) {
+  // K(t) into registers (widened by store_tile); V(t) straight into its stage's LDS: load
+  // r of wave w fills LDS chunks idx = r NT + 64 w + lane, i.e. (row idx / CPR, chunk
+  // idx % CPR), from the row's key and swizzled chunk.
+  auto load_tile = [&](int t, int stage) {
     const int k0 = t * BC;
 #pragma unroll
     for (int r = 0; r < K_LOADS; ++r) {
@@ -159,22 +179,22 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       if (idx < BC * D / 16 && key < a.Sk) val = ld_global_16(kb + (int64_t)key * D + c16 * 16);
       kreg[r] = val;
     }
-    if (tid < V_BLOCKS) {
-      const int kq = tid / (D / 16);
-      const int dc = tid % (D / 16);
+    const uint32_t vdst = lds_offset(lds + stage * L::STAGE + L::K_BYTES);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = k0 + 4 * kq + s;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (key < a.Sk) val = ld_global_16(vb + (int64_t)key * D + dc * 16);
-        vreg[s] = val;
+    for (int r = 0; r < V_LOADS; ++r) {
+      const int idx0 = r * NT + w * kWave;   // wave-uniform
+      if (idx0 < BC * CPR) {
+        const int idx = idx0 + lane;
+        const int row = idx / CPR, pos = idx % CPR;
+        lds_load_16(vrs, (uint32_t)(v_row_key(row) * D + (pos ^ v_swz<D>(row)) * 16),
+                    (uint32_t)(__builtin_amdgcn_readfirstlane(t) * BC * D),
+                    __builtin_amdgcn_readfirstlane(vdst + idx0 * 16));
       }
     }
   };
 
   auto store_tile = [&](int stage) {
     uint8_t* ks = lds + stage * L::STAGE;
-    uint8_t* vs = ks + L::K_BYTES;
 #pragma unroll
     for (int r = 0; r < K_LOADS; ++r) {
       const int idx = r * NT + tid;
@@ -186,105 +206,108 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         st_lds_16(kd + 8, e4m3x8_to_bf16(kreg[r].z, kreg[r].w));
       }
     }
-    if (tid < V_BLOCKS) {
-      const int kq = tid / (D / 16);
-      const int dc = tid % (D / 16);
-      const int pos = vt_pos(4 * kq);
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        // 4 keys x 4 d bytes -> 4 dwords, each holding the 4 keys of one d column
-        const uint32_t r0 = vreg[0][wd], r1 = vreg[1][wd], r2 = vreg[2][wd], r3 = vreg[3][wd];
-        const uint32_t lo01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-        const uint32_t c0 = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-        const uint32_t c1 = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-        const uint32_t c2 = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-        const uint32_t c3 = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
-        const int d0 = dc * 16 + 4 * wd;
-        *reinterpret_cast<uint32_t*>(vs + (d0 + 0) * L::VSTR + pos) = c0;
-        *reinterpret_cast<uint32_t*>(vs + (d0 + 1) * L::VSTR + pos) = c1;
-        *reinterpret_cast<uint32_t*>(vs + (d0 + 2) * L::VSTR + pos) = c2;
-        *reinterpret_cast<uint32_t*>(vs + (d0 + 3) * L::VSTR + pos) = c3;
-      }
-    }
   };
 
-  // One K/V tile.  MASKED applies the key-tail mask (only the tiles the plan marks).
-  auto compute_tile = [&](auto masked_tag, int t, int stage) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const uint8_t* ks = lds + stage * L::STAGE;
-    const uint8_t* vs = ks + L::K_BYTES;
-    const float dk = ksc[(t * BC) / SCALE_ROWS];
-    const float dv = vsc[(t * BC) / SCALE_ROWS];
-    f32x16 s[2];
-    const bf16* kbf = reinterpret_cast<const bf16*>(ks);
+  // Software pipeline (as in the 16-bit forward): step t issues the score product of
+  // tile t+1 chunk by chunk between the exponentials of tile t, so that each chunk's
+  // vector work runs while the matrix core works on independent products; then the
+  // accumulator rescale and the P V product of tile t, the staging of tile t+2, and the
+  // row max of tile t+1.  Tiles live in kStages LDS stages: step t reads K(t+1) and
+  // V(t) and writes tile t+2 into the stage tile t-1 held, so one barrier per step
+  // publishes the writes and frees the next stage.  Every element goes through the same
+  // arithmetic in the same order as a tile-at-a-time schedule.
+  constexpr int KC = D / 16;                 // contraction chunks of the score product
+  constexpr int NCH = 4;                     // pipeline chunks per tile
+  constexpr int KPC = KC / NCH;              // score chunks per pipeline chunk
+  constexpr int PPC = 16 / NCH;              // exponential pairs per pipeline chunk
+  static_assert(KPC * NCH == KC, "the score chunks split evenly");
+
+  // The tile whose probabilities come next: its score factor, the frame m its values
+  // u = 2^8 exp2(x - m) are taken in, and the factor that moves l into that frame.
+  float p_csc = 0.f, p_moff = 0.f, p_alpha = 1.f, p_mnew = -INFINITY;
+
+  auto qk_part = [&](f32x16 (&sc)[2], int stage, int kc0, int kc1) {
+    const bf16* kbf = reinterpret_cast<const bf16*>(lds + stage * L::STAGE);
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
+    for (int kc = kc0; kc < kc1; ++kc) {
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
         const bf16x8 av = as_v8<bf16x8>(ld_lds_16(kbf + (kbk * 32 + n) * L::KSTR + 16 * kc + 8 * grp));
-        s[kbk] = Elem<bf16>::mfma(av, qf[kc], kc == 0 ? f32x16{} : s[kbk]);
+        sc[kbk] = Elem<bf16>::mfma(av, qf[kc], kc == 0 ? f32x16{} : sc[kbk]);
       }
       if ((kc & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
     }
-    // Descales before the row max: x = csc * s with csc = scale log2(e) dQ dK.  The max
-    // is taken on the raw accumulators (csc >= 0: descales are positive and a negative
-    // score scale is moved into Q), so x enters only through one FMA below.
-    const float csc = c_q * dk;
-    // visibility of register i of key block kbk: its key offset against this lane's
-    // limit (the per-register offsets are constants, one compare each)
-    const int lim = klim - t * BC - 4 * grp;
-    auto vis = [&](int kbk, int i) { return !MASKED || (kbk * 32 + 8 * (i >> 2) + (i & 3)) < lim; };
-    if constexpr (MASKED) {
+  };
+
+  // Descales before the row max: x = csc * s with csc = scale log2(e) dQ dK.  The max is
+  // taken on the raw accumulators (csc >= 0: descales are positive and a negative score
+  // scale is moved into Q), so x enters only through one FMA in the exponentials.
+  // MASKED sets the invisible scores to -inf first (only the tiles the plan marks).
+  auto prepare = [&](f32x16 (&sc)[2], int t, bool masked) {
+    const float dk = ksc[(t * BC) / SCALE_ROWS];
+    if (masked) {
+      // visibility of register i of key block kbk: its key offset against this lane's
+      // limit (the per-register offsets are constants, one compare each)
+      const int lim = klim - t * BC - 4 * grp;
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kbk][i] = vis(kbk, i) ? s[kbk][i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) sc[kbk][i] = (kbk * 32 + 8 * (i >> 2) + (i & 3)) < lim ? sc[kbk][i] : -INFINITY;
     }
-    float r0 = vmax(s[0][0], s[0][1]), r1 = vmax(s[0][2], s[0][3]);
+    float r0 = vmax(sc[0][0], sc[0][1]), r1 = vmax(sc[0][2], sc[0][3]);
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
       for (int i = (kbk == 0 ? 4 : 0); i < 16; i += 4) {
-        r0 = vmax(r0, vmax(s[kbk][i], s[kbk][i + 1]));
-        r1 = vmax(r1, vmax(s[kbk][i + 2], s[kbk][i + 3]));
+        r0 = vmax(r0, vmax(sc[kbk][i], sc[kbk][i + 1]));
+        r1 = vmax(r1, vmax(sc[kbk][i + 2], sc[kbk][i + 3]));
       }
     const float mr = vmax(r0, r1);
+    const float csc = c_q * dk;
     const float mx = max_pair32(mr == -INFINITY ? -INFINITY : mr * csc);
     const float m_new = fmaxf(m_i, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_i - m_use);
-    const float m_off = m_use - 8.f;                 // u = 2^8 exp2(x - m)
-    float rs0 = 0.f, rs1 = 0.f;
+    p_alpha = fast_exp2(m_i - m_use);
+    p_moff = m_use - 8.f;                    // u = 2^8 exp2(x - m)
+    p_csc = csc;
+    p_mnew = m_new;
+  };
+
+  // Exponential pairs PPC c .. PPC (c+1) - 1 of tile t (pair p: key block p / 8,
+  // registers 2 (p % 8) and + 1), their sums in rs0 (even registers) and rs1 (odd).
+  auto exp_part = [&](auto masked_tag, f32x16 (&sc)[2], int t, int c, float& rs0, float& rs1) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int lim = klim - t * BC - 4 * grp;
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        // masked cells give u = 0 by selection (a zero descale or scale makes csc = 0,
-        // and fma(-inf, 0, .) would be NaN)
-        float u0 = fast_exp2(fmaf(s[kbk][i], csc, -m_off));
-        float u1 = fast_exp2(fmaf(s[kbk][i + 1], csc, -m_off));
-        if constexpr (MASKED) {
-          u0 = vis(kbk, i) ? u0 : 0.f;
-          u1 = vis(kbk, i + 1) ? u1 : 0.f;
-        }
-        s[kbk][i] = u0;
-        s[kbk][i + 1] = u1;
-        rs0 += u0;
-        rs1 += u1;
+    for (int pr = PPC * c; pr < PPC * (c + 1); ++pr) {
+      const int kbk = pr >> 3, i = 2 * (pr & 7);
+      // masked cells give u = 0 by selection (a zero descale or scale makes csc = 0,
+      // and fma(-inf, 0, .) would be NaN)
+      float u0 = fast_exp2(fmaf(sc[kbk][i], p_csc, -p_moff));
+      float u1 = fast_exp2(fmaf(sc[kbk][i + 1], p_csc, -p_moff));
+      if constexpr (MASKED) {
+        u0 = (kbk * 32 + 8 * (i >> 2) + (i & 3)) < lim ? u0 : 0.f;
+        u1 = (kbk * 32 + 8 * ((i + 1) >> 2) + ((i + 1) & 3)) < lim ? u1 : 0.f;
       }
+      sc[kbk][i] = u0;
+      sc[kbk][i + 1] = u1;
+      rs0 += u0;
+      rs1 += u1;
     }
-    l_i = alpha * l_i + (rs0 + rs1);
-    m_i = m_new;
+  };
+
+  // The running state moves to tile t's frame, then O takes tile t's P V product.
+  auto finish = [&](f32x16 (&sc)[2], int t, int stage, float rs0, float rs1) {
+    l_i = p_alpha * l_i + (rs0 + rs1);
+    m_i = p_mnew;
+    const float dv = vsc[(t * BC) / SCALE_ROWS];
     // The accumulator is kept in units of the current V descale s_v: moving to a tile
     // with descale dv (and a moved max) multiplies it by alpha s_v / dv, skipped when
     // that is 1 in every lane (same scale block, unmoved max).  A zero V descale (an
     // all-zero value block) makes the tile's values zero: the accumulator keeps its
     // frame and the tile adds nothing (dv is the same for every lane of the workgroup).
     const bool v_zero = !(dv != 0.f);
-    const float beta = v_zero ? alpha : alpha * (s_v / dv);
+    const float beta = v_zero ? p_alpha : p_alpha * (s_v / dv);
     if (!v_zero) s_v = dv;
     if (wave_any(beta != 1.f)) {
 #pragma unroll
@@ -293,7 +316,6 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         for (int i = 0; i < 16; ++i) o[db][i] *= beta;
       }
     }
-    // A zero-valued tile adds nothing in the current frame (dv is the same in every lane).
     if (v_zero) return;
     // P^T as the fp8 B operand: slot j = register (j % 16) of key block j / 16.
     i32x8 pb;
@@ -301,38 +323,96 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
     for (int wd = 0; wd < 8; ++wd) {
       const int kbk = wd >> 2;
       const int i0 = 4 * (wd & 3);
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[kbk][i0], s[kbk][i0 + 1], 0, false);
-      v = __builtin_amdgcn_cvt_pk_fp8_f32(s[kbk][i0 + 2], s[kbk][i0 + 3], v, true);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(sc[kbk][i0], sc[kbk][i0 + 1], 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(sc[kbk][i0 + 2], sc[kbk][i0 + 3], v, true);
       pb[wd] = v;
     }
+    // V^T (d row 32 db + n, slots 8m .. 8m+7 = LDS rows 16m + 8 grp .. +7) by transpose
+    // reads: lane s of a 16-lane group addresses row s / 2 of the 8, half s % 2 of the
+    // d chunk 2 db + (n / 16)
+    const uint8_t* vs = lds + stage * L::STAGE + L::K_BYTES;
+    const int s16 = lane & 15;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint8_t* vr = vs + (db * 32 + n) * L::VSTR + 32 * grp;
-      const u32x4 lo = ld_lds_16(vr), hi = ld_lds_16(vr + 16);
-      const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const int cch = 2 * db + (n >> 4);
+      i32x8 av;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = 16 * m + 8 * grp + (s16 >> 1);
+        const u32x2 r = tr8_read(vs + row * D + ((cch ^ v_swz<D>(row)) * 16) + 8 * (s16 & 1));
+        av[2 * m] = (int)r.x;
+        av[2 * m + 1] = (int)r.y;
+      }
       o[db] = mfma_fp8(av, pb, o[db]);
     }
   };
 
+  // One step: tile t is in `cur` (scored, prepared), tile t+1 is scored into `nxt`.  A
+  // wave whose rows see nothing of a tile (causal band) skips its work; every wave
+  // still stages and passes the barrier.
   const int nt = plan.n_visit;
+  const int wn = wplan.n_visit;
+  auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    const bool has_new = t + 2 < nt;
+    if (has_new) load_tile(t + 2, (t + 2) % kStages);
+    const bool has_cur = t < wn, has_nxt = t + 1 < wn;
+    const int s_cur = t % kStages, s_nxt = (t + 1) % kStages;
+    float rs0 = 0.f, rs1 = 0.f;
+    const bool masked = t >= wplan.first_masked;
+    if (has_cur && has_nxt) {
+      if (masked) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          __builtin_amdgcn_s_setprio(1);
+          qk_part(nxt, s_nxt, c * KPC, (c + 1) * KPC);
+          __builtin_amdgcn_s_setprio(0);
+          exp_part(std::true_type{}, cur, t, c, rs0, rs1);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          __builtin_amdgcn_s_setprio(1);
+          qk_part(nxt, s_nxt, c * KPC, (c + 1) * KPC);
+          __builtin_amdgcn_s_setprio(0);
+          exp_part(std::false_type{}, cur, t, c, rs0, rs1);
+        }
+      }
+    } else if (has_cur) {
+      if (masked) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) exp_part(std::true_type{}, cur, t, c, rs0, rs1);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) exp_part(std::false_type{}, cur, t, c, rs0, rs1);
+      }
+    } else if (has_nxt) {
+      qk_part(nxt, s_nxt, 0, KC);
+    }
+    if (has_cur) finish(cur, t, s_cur, rs0, rs1);
+    if (has_new) store_tile((t + 2) % kStages);
+    if (has_nxt) prepare(nxt, t + 1, t + 1 >= wplan.first_masked);
+    wait_vmcnt<0>();                         // this thread's direct V loads have landed
+    __syncthreads();
+  };
+
   if (nt > 0) {
-    load_tile(0);
+    load_tile(0, 0);
     store_tile(0);
   }
+  if (nt > 1) {
+    load_tile(1, 1);
+    store_tile(1);
+  }
+  wait_vmcnt<0>();
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    // a wave whose rows see nothing of tile t (causal band) skips it; every wave still
-    // stages and passes the barrier
-    if (t < wplan.n_visit) {
-      if (t >= wplan.first_masked)
-        compute_tile(std::true_type{}, t, stage);
-      else
-        compute_tile(std::false_type{}, t, stage);
-    }
-    if (t + 1 < nt) store_tile(stage ^ 1);
-    __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (wn > 0) {
+    qk_part(sa, 0, 0, KC);
+    prepare(sa, 0, 0 >= wplan.first_masked);
+  }
+  for (int t = 0; t < nt; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < nt) step(t + 1, sb, sa);
   }
 
   const float l_tot = l_i + __shfl_xor(l_i, 32);
