@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   // publishes the writes and frees the next stage.  Every element goes through the same
   // arithmetic in the same order as a tile-at-a-time schedule.
   constexpr int KC = D / 16;                 // contraction chunks of the score product
-  constexpr int NCH = 4;                     // pipeline chunks per tile
+  constexpr int NCH = D == 128 ? 8 : 4;     // pipeline chunks per tile (one or two score chunks)
   constexpr int KPC = KC / NCH;              // score chunks per pipeline chunk
   constexpr int PPC = 16 / NCH;              // exponential pairs per pipeline chunk
   static_assert(KPC * NCH == KC, "the score chunks split evenly");
@@ -363,17 +363,13 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       if (masked) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          __builtin_amdgcn_s_setprio(1);
           qk_part(nxt, s_nxt, c * KPC, (c + 1) * KPC);
-          __builtin_amdgcn_s_setprio(0);
           exp_part(std::true_type{}, cur, t, c, rs0, rs1);
         }
       } else {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          __builtin_amdgcn_s_setprio(1);
           qk_part(nxt, s_nxt, c * KPC, (c + 1) * KPC);
-          __builtin_amdgcn_s_setprio(0);
           exp_part(std::false_type{}, cur, t, c, rs0, rs1);
         }
       }
