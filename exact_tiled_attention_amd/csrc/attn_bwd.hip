@@ -158,27 +158,31 @@ __device__ inline u32x4 e4m3x8_bf16(const u32x2& w) {
 // dS goes to LDS key-major and the eight waves compute dQ = dS K in 16x16 tiles over
 // the tile's 128 keys (transpose reads of dS and of the K tile kept in LDS), added
 // with float32 atomics ([FA2] section 0x06.1F).  Q and dO tiles go straight from
-// HBM/L2 into LDS (two slots, one step ahead).  dS has two slots, so the dQ tiles of
-// step t run at the start of step t + 1, after its first barrier: two barriers per step
-// (staged tiles and the previous dS visible; P visible), and the atomics are issued a
-// whole step before the wait that precedes the next barrier.
+// HBM/L2 into LDS (one step ahead).  dS has two slots, so the dQ tiles of step t run at
+// the start of step t + 1, after its first barrier: two barriers per step (staged tiles
+// and the previous dS visible; P visible), and the atomics are issued a whole step
+// before the wait that precedes the next barrier.  Without dQ (and with 16-bit operands
+// and no dropout) the dS waves lag one query tile behind the P waves instead: step k
+// runs S, P and dV of tile k and dP, dS and dK of tile k - 1, one barrier per step.
 constexpr int kKW = 32;               // keys per group
 constexpr int kKG = 4;                // key groups per workgroup
 constexpr int kKVT = kKW * kKG;       // keys per workgroup
 constexpr int kKVW = 2 * kKG;         // waves per workgroup
 constexpr int kKVQ = 32;              // queries per step
 
-template <int D>
+// QS staged Q / dO slots and PSL P-handoff slots (3 and 2 in the lagged schedule).
+template <int D, int QS, int PSL>
 struct KvLds {
   static constexpr int ROWB = D * 2;
   static constexpr int QT = kKVQ * ROWB;            // one staged Q or dO tile
-  static constexpr int Q0 = 0;                      // Q slots 0, 1
-  static constexpr int DO0 = 2 * QT;                // dO slots 0, 1
-  static constexpr int K = 4 * QT;                  // K tile [128 keys][D]
+  static constexpr int Q0 = 0;                      // Q slots
+  static constexpr int DO0 = QS * QT;               // dO slots
+  static constexpr int K = 2 * QS * QT;             // K tile [128 keys][D]
   static constexpr int DS = K + kKVT * ROWB;        // dS slots 0, 1: [128 keys][32 queries], 64-byte rows
   static constexpr int DSS = 2 * kKVT * kKVQ * 2;   // one slot: the values, then their bf16 residuals
-  static constexpr int P = DS + 2 * DSS;            // P handoff [group][16 registers][64 lanes] float32
-  static constexpr int Z = P + kKG * 16 * kWave * 4; // dropout keep bits [role][group][64 lanes] uint32
+  static constexpr int P = DS + 2 * DSS;            // P handoff [slot][group][16 registers][64 lanes] float32
+  static constexpr int PS = kKG * 16 * kWave * 4;   // one P slot
+  static constexpr int Z = P + PSL * PS;            // dropout keep bits [role][group][64 lanes] uint32
   static constexpr int BYTES = Z + 2 * kKG * kWave * 4;
 };
 
@@ -213,7 +217,12 @@ void bwd_kv_kernel(BwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
   typedef M16<T> MF;
-  typedef KvLds<D> L;
+  // Lagged schedule (no dQ, 16-bit operands, no dropout): in step k the P waves take
+  // query tile k (S, P, dV) while the dS waves take tile k - 1 (dP, dS, dK) with the P
+  // their partners handed over a step earlier, so the two roles no longer wait for each
+  // other within a step: one barrier per step, three Q / dO slots, two P slots.
+  constexpr bool LAG = !DQ && !F8 && !DROP;
+  typedef KvLds<D, LAG ? 3 : 2, LAG ? 2 : 1> L;
   constexpr int KC = D / 16;                 // contraction chunks of S and dP
   constexpr int DB = D / 32;                 // 32-wide d blocks of dK, dV
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -222,8 +231,8 @@ void bwd_kv_kernel(BwdArgs a) {
   static_assert(WL * kWave == kKVQ * CPR && kWave % CPR == 0, "staging splits evenly");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][kKVQ];
-  __shared__ __attribute__((aligned(16))) float s_del[2][kKVQ];
+  __shared__ __attribute__((aligned(16))) float s_lse[LAG ? 3 : 2][kKVQ];
+  __shared__ __attribute__((aligned(16))) float s_del[LAG ? 3 : 2][kKVQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -355,7 +364,7 @@ void bwd_kv_kernel(BwdArgs a) {
     const int col = c0 + 4 * (s16 & 3);
     return tr_read(tile + r * L::ROWB + (((col >> 3) ^ kv_swz<D>(r)) * 16) + (col & 7) * 2);
   };
-  float* phand = reinterpret_cast<float*>(lds + L::P) + grp * 16 * kWave + lane;   // [reg][lane]
+  float* const phand0 = reinterpret_cast<float*>(lds + L::P) + grp * 16 * kWave + lane;   // [reg][lane]
   uint32_t* zhand = reinterpret_cast<uint32_t*>(lds + L::Z) + grp * kWave + lane;  // [role][group][lane]
   uint32_t keep = 0;                         // dropout: this step's decisions (bit i = register i)
   int h_cur = 0;                             // this step's query head (the dropout counter)
@@ -363,8 +372,9 @@ void bwd_kv_kernel(BwdArgs a) {
   // Phase 1: S (role P) or dP (role dS) for the group's 32 keys: A = Q / dO rows (row n,
   // chunk 2kc + g) of the staged tile, B = the group's K / V fragments.  Role P turns S
   // into P (masked) and hands it to its partner.
-  auto phase1 = [&](auto masked_tag, int qt, int sb, float sl2, f32x16& x) {
+  auto phase1 = [&](auto masked_tag, int qt, int sb, float sl2, f32x16& x, int ps) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    float* const phand = phand0 + ps * (L::PS / 4);
     const uint8_t* src = lds + (role_p ? L::Q0 : L::DO0) + sb * L::QT;
     x = f32x16{};
 #pragma unroll
@@ -429,7 +439,8 @@ void bwd_kv_kernel(BwdArgs a) {
   // Chunk c: A = registers 8c .. 8c+7 (queries 16c + 4g + s%4 and 16c + 8 + 4g + s%4),
   // B = dO / Q columns by transpose reads of those rows; bf16 carries P and dS as
   // hi + lo pairs.
-  auto phase2 = [&](int sb, float dq_s, f32x16& x) {
+  auto phase2 = [&](int sb, float dq_s, f32x16& x, int ps) {
+    const float* const phand = phand0 + ps * (L::PS / 4);
     uint8_t* dsv = lds + L::DS + sb * L::DSS;
     uint8_t* dsr = dsv + L::DSS / 2;
     const uint8_t* src = lds + (role_p ? L::DO0 : L::Q0) + sb * L::QT;
@@ -535,45 +546,80 @@ void bwd_kv_kernel(BwdArgs a) {
     store_q(0);
     fetch_rows(0);
   }
-  // With DQ one more pass runs the last step's dQ tiles.
-  const int npass = (DQ && nsteps > 0) ? nsteps + 1 : nsteps;
-  int ph = 0, pqt = 0;                       // the previous step's head and query tile
-  for (int step = 0; step < npass; ++step) {
-    const bool work = step < nsteps;
-    int h = 0, qt = 0;
-    if (work) step_coords(step, h, qt);
-    h_cur = h;
-    const int sb = step & 1;
-    if (work) store_rows(sb);
-    // this step's tiles have landed (own loads) and, after the barrier, everyone's;
-    // every wave has finished step - 1 (its P handoff, its dS writes, and the staged
-    // slot the loads below overwrite)
+  if constexpr (LAG) {
+    // Step k: the rows of tile k are stored and tile k has landed; after the barrier
+    // every wave has finished step k - 1 (P(k - 1) is visible, and the Q / dO slot of
+    // tile k - 2 is free for tile k + 1).
+    for (int k = 0; k <= nsteps; ++k) {
+      if (k < nsteps) store_rows(k % 3);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (k + 1 < nsteps) {
+        stage(k + 1, (k + 1) % 3);
+        fetch_rows(k + 1);
+      }
+      if (role_p) {
+        if (k < nsteps) {
+          int h, qt;
+          step_coords(k, h, qt);
+          const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
+          f32x16 x;
+          if (masked)
+            phase1(std::true_type{}, qt, k % 3, sl2b, x, k & 1);
+          else
+            phase1(std::false_type{}, qt, k % 3, sl2b, x, k & 1);
+          phase2(k % 3, 1.f, x, k & 1);
+        }
+      } else if (k >= 1) {
+        int h, qt;
+        step_coords(k - 1, h, qt);
+        f32x16 x;
+        phase1(std::false_type{}, qt, (k - 1) % 3, sl2b, x, (k - 1) & 1);   // dP (P carries the mask)
+        phase2((k - 1) % 3, 1.f, x, (k - 1) & 1);
+      }
+    }
     wait_vmcnt<0>();
-    __syncthreads();
-    if (step + 1 < nsteps) {
-      stage(step + 1, sb ^ 1);
-      fetch_rows(step + 1);
+  } else {
+    // With DQ one more pass runs the last step's dQ tiles.
+    const int npass = (DQ && nsteps > 0) ? nsteps + 1 : nsteps;
+    int ph = 0, pqt = 0;                       // the previous step's head and query tile
+    for (int step = 0; step < npass; ++step) {
+      const bool work = step < nsteps;
+      int h = 0, qt = 0;
+      if (work) step_coords(step, h, qt);
+      h_cur = h;
+      const int sb = step & 1;
+      if (work) store_rows(sb);
+      // this step's tiles have landed (own loads) and, after the barrier, everyone's;
+      // every wave has finished step - 1 (its P handoff, its dS writes, and the staged
+      // slot the loads below overwrite)
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (step + 1 < nsteps) {
+        stage(step + 1, sb ^ 1);
+        fetch_rows(step + 1);
+      }
+      if constexpr (DQ) {
+        if (step > 0) phase3(ph, pqt, sb ^ 1);
+      }
+      if (work) {
+        const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
+        const float dq_s = q_descale(h, qt);
+        const float sl2 = F8 ? a.scale_log2 * dq_s * dk_s : sl2b;
+        f32x16 x;
+        if (masked)
+          phase1(std::true_type{}, qt, sb, sl2, x, 0);
+        else
+          phase1(std::false_type{}, qt, sb, sl2, x, 0);
+        __syncthreads();                       // P of every group visible
+        phase2(sb, dq_s, x, 0);
+      }
+      if (step + 1 < nsteps) store_q(sb ^ 1);  // fp8: the next step's Q, widened
+      ph = h;
+      pqt = qt;
     }
-    if constexpr (DQ) {
-      if (step > 0) phase3(ph, pqt, sb ^ 1);
-    }
-    if (work) {
-      const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
-      const float dq_s = q_descale(h, qt);
-      const float sl2 = F8 ? a.scale_log2 * dq_s * dk_s : sl2b;
-      f32x16 x;
-      if (masked)
-        phase1(std::true_type{}, qt, sb, sl2, x);
-      else
-        phase1(std::false_type{}, qt, sb, sl2, x);
-      __syncthreads();                       // P of every group visible
-      phase2(sb, dq_s, x);
-    }
-    if (step + 1 < nsteps) store_q(sb ^ 1);  // fp8: the next step's Q, widened
-    ph = h;
-    pqt = qt;
+    wait_vmcnt<0>();
   }
-  wait_vmcnt<0>();
 
   // dV = sum P^T dO (role P), dK = scale sum dS^T Q (role dS); lane = d column 32db + n,
   // register i = key 8(i/4) + 4g + i%4 of the group's 32
