@@ -41,6 +41,8 @@ def _check(w, dq_splits):
     (1, 8, 2, 200, 333),      # S_q < S_k, GQA 4
     (1, 2, 2, 300, 100),      # S_q > S_k: causal rows with no visible key
     (1, 4, 2, 70, 1),         # one key
+    (1, 2, 2, 32, 96),        # one query tile: the column owner's loop has one step
+    (1, 2, 2, 64, 64),        # two steps
 ])
 def test_deterministic_elementwise(dtype, d, causal, B, Hq, Hkv, Sq, Sk):
     need_gpu()

@@ -62,7 +62,10 @@ def _check(w, rows=None, heads=None, causal=False, scale=None):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk", [(1, 2, 2, 128, 128), (2, 4, 2, 200, 333), (1, 2, 1, 64, 1),
-                                            (1, 1, 1, 300, 64), (1, 2, 2, 300, 100)])
+                                            (1, 1, 1, 300, 64), (1, 2, 2, 300, 100),
+                                            # three and four key tiles: every slot of the
+                                            # three-stage K/V ring, and its first reuse
+                                            (1, 2, 2, 150, 150), (1, 2, 1, 100, 250)])
 def test_fp8_small_elementwise(d, causal, B, Hq, Hkv, Sq, Sk):
     need_gpu()
     _check(attn_inputs.fp8_prefill(B, Hq, Hkv, Sq, Sk, d, seed=500 + Sq + Sk + d), causal=causal)
