@@ -705,9 +705,10 @@ void bwd_dq_kernel(BwdArgs a) {
   const int tb = min(plan.n_visit, split * per);
   const int te = min(plan.n_visit, tb + per);
 
-  // swizzle of the 16-byte chunks of a staged row (16 consecutive rows on distinct
-  // bank groups for the fragment reads)
-  auto swz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  // swizzle of the 16-byte chunks of a staged row: 16 consecutive rows on distinct
+  // bank groups for the fragment reads and, at d = 128, the transpose reads of the dQ
+  // product (4 rows x 2 chunks) on 8 distinct positions too, as in the column owner
+  auto swz = [](int r) { return D == 128 ? kv_swz<128>(r) : ((r >> 1) & 7); };
 
   const int64_t rowq0 = (int64_t)(b * a.Hq + h) * a.Sq;
   const T* qb = reinterpret_cast<const T*>(a.q) + rowq0 * D;
