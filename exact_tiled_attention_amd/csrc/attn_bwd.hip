@@ -307,9 +307,7 @@ void bwd_kv_kernel(BwdArgs a) {
   // stage() and widened into the LDS slot by store_q()
   constexpr int Q8C = kKVQ * D / 8;          // 8-byte chunks of a Q8 tile
   u32x2 q8 = {0u, 0u};
-  auto stage = [&](int step, int sb) {
-    int h, qt;
-    step_coords(step, h, qt);
+  auto stage_at = [&](int h, int qt, int sb) {
     const int64_t base = ((int64_t)(b * a.Hq + h) * a.Sq) * D;
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const uint8_t*>(a.q) + base * EB, (uint32_t)a.Sq * D * EB);
     const __amdgpu_buffer_rsrc_t dr = make_rsrc(reinterpret_cast<const T*>(a.dO) + base, (uint32_t)a.Sq * D * 2);
@@ -327,6 +325,11 @@ void bwd_kv_kernel(BwdArgs a) {
       if (tid < Q8C) q8 = buf_load_8(qr, (uint32_t)((qt * kKVQ + tid / (D / 8)) * D + 8 * (tid % (D / 8))));
     }
   };
+  auto stage = [&](int step, int sb) {
+    int h, qt;
+    step_coords(step, h, qt);
+    stage_at(h, qt, sb);
+  };
   auto store_q = [&](int sb) {
     if constexpr (F8) {
       if (tid < Q8C) {
@@ -342,14 +345,17 @@ void bwd_kv_kernel(BwdArgs a) {
   };
   // LSE (base 2) and D of the step's rows, through registers
   float pre = 0.f;
-  auto fetch_rows = [&](int step) {
+  auto fetch_rows_at = [&](int h, int qt) {
     if (tid < 2 * kKVQ) {
-      int h, qt;
-      step_coords(step, h, qt);
       const int qr = qt * kKVQ + (tid & (kKVQ - 1));
       const int64_t ri = (int64_t)(b * a.Hq + h) * a.Sq + qr;
       pre = qr < a.Sq ? (tid < kKVQ ? a.lse[ri] * ATTN_LOG2E : a.delta[ri]) : (tid < kKVQ ? INFINITY : 0.f);
     }
+  };
+  auto fetch_rows = [&](int step) {
+    int h, qt;
+    step_coords(step, h, qt);
+    fetch_rows_at(h, qt);
   };
   auto store_rows = [&](int sb) {
     if (tid < kKVQ) s_lse[sb][tid] = pre;
@@ -550,18 +556,29 @@ void bwd_kv_kernel(BwdArgs a) {
     // Step k: the rows of tile k are stored and tile k has landed; after the barrier
     // every wave has finished step k - 1 (P(k - 1) is visible, and the Q / dO slot of
     // tile k - 2 is free for tile k + 1).
+    // coordinates of steps k - 1, k and k + 1, advanced without divisions
+    int qt_prev = 0, h_k = 0, qt_k = 0, h_next = 0, qt_next = 0;
+    if (nsteps > 0) step_coords(0, h_k, qt_k);
+    auto advance = [&](int& h, int& qt) {
+      if (++qt == cp.n_qtiles) {
+        qt = cp.first_qtile;
+        ++h;
+      }
+    };
+    h_next = h_k;
+    qt_next = qt_k;
+    advance(h_next, qt_next);
     for (int k = 0; k <= nsteps; ++k) {
       if (k < nsteps) store_rows(k % 3);
       wait_vmcnt<0>();
       __syncthreads();
       if (k + 1 < nsteps) {
-        stage(k + 1, (k + 1) % 3);
-        fetch_rows(k + 1);
+        stage_at(h_next, qt_next, (k + 1) % 3);
+        fetch_rows_at(h_next, qt_next);
       }
       if (role_p) {
         if (k < nsteps) {
-          int h, qt;
-          step_coords(k, h, qt);
+          const int h = h_k, qt = qt_k;
           const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
           f32x16 x;
           if (masked)
@@ -571,12 +588,14 @@ void bwd_kv_kernel(BwdArgs a) {
           phase2(k % 3, 1.f, x, k & 1);
         }
       } else if (k >= 1) {
-        int h, qt;
-        step_coords(k - 1, h, qt);
         f32x16 x;
-        phase1(std::false_type{}, qt, (k - 1) % 3, sl2b, x, (k - 1) & 1);   // dP (P carries the mask)
+        phase1(std::false_type{}, qt_prev, (k - 1) % 3, sl2b, x, (k - 1) & 1);   // dP (P carries the mask)
         phase2((k - 1) % 3, 1.f, x, (k - 1) & 1);
       }
+      qt_prev = qt_k;
+      h_k = h_next;
+      qt_k = qt_next;
+      advance(h_next, qt_next);
     }
     wait_vmcnt<0>();
   } else {
