@@ -125,7 +125,7 @@ void fwd_kernel(FwdArgs a) {
   static_assert(TL::CHUNKS % NTK == 0 && LOADS >= 1, "chunks must split evenly over the threads");
   static_assert(KC % PC == 0, "score product must split evenly over the key chunks");
   constexpr int NV = 2 + 16 * DB;             // merged values per lane and query block
-  constexpr int MERGE = RW * QB * NV * kWave * 4;
+  constexpr int MERGE = (KS - 1) * RW * QB * NV * kWave * 4;   // states of key ranges 1 .. KS-1
   constexpr int LDS = (KS > 1 && MERGE > KS * RING) ? MERGE : KS * RING;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_all[LDS];
@@ -552,41 +552,52 @@ void fwd_kernel(FwdArgs a) {
   wait_vmcnt<0>();   // no ring load may still be in flight when the LDS is reused
   if constexpr (KS > 1) {
     // Merge the key ranges' states of each row in one max frame ("M4.3 - IO-Aware
-    // Attention ...", section 0x08B): range r hands its (m, l, u) to range 0 through
-    // LDS, one range per round.  Layout [wave][block][value][lane] keeps lanes on banks.
+    // Attention ...", section 0x08B): ranges 1 .. KS-1 hand their (m, l, u) to range 0
+    // through LDS, all at once, and range 0 combines them.  Layout
+    // [range][wave][block][value][lane] keeps lanes on banks.
     float* xf = reinterpret_cast<float*>(lds_all);
-#pragma unroll
-    for (int r = 1; r < KS; ++r) {
-      __syncthreads();                                 // the ring / previous round is free
+    __syncthreads();                                   // the rings are free
+    if (kh > 0) {
 #pragma unroll
       for (int j = 0; j < QB; ++j) {
-        float* slot = xf + ((w * QB + j) * NV) * kWave + lane;
-        if (kh == r) {
-          slot[0] = m_i[j];
-          slot[kWave] = l_i[j];
+        float* slot = xf + (((kh - 1) * RW + w) * QB + j) * NV * kWave + lane;
+        slot[0] = m_i[j];
+        slot[kWave] = l_i[j];
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) slot[(2 + 16 * db + q) * kWave] = o[j][db][q];
-        }
+          for (int q = 0; q < 16; ++q) slot[(2 + 16 * db + q) * kWave] = o[j][db][q];
       }
-      __syncthreads();
-      if (kh == 0) {
+    }
+    __syncthreads();
+    if (kh == 0) {
 #pragma unroll
-        for (int j = 0; j < QB; ++j) {
-          const float* slot = xf + ((w * QB + j) * NV) * kWave + lane;
-          const float m1 = slot[0];
-          const float l1 = slot[kWave];
-          const float m = fmaxf(m_i[j], m1);
-          const float a0 = (m == -INFINITY) ? 0.f : fast_exp2(m_i[j] - m);
-          const float a1 = (m == -INFINITY) ? 0.f : fast_exp2(m1 - m);
-          l_i[j] = a0 * l_i[j] + a1 * l1;
+      for (int j = 0; j < QB; ++j) {
+        float mr[KS], sc[KS];
+        mr[0] = m_i[j];
+        float m = m_i[j];
+#pragma unroll
+        for (int r = 1; r < KS; ++r) {
+          mr[r] = xf[(((r - 1) * RW + w) * QB + j) * NV * kWave + lane];
+          m = fmaxf(m, mr[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < KS; ++r) sc[r] = (m == -INFINITY) ? 0.f : fast_exp2(mr[r] - m);
+        l_i[j] *= sc[0];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) o[j][db][q] *= sc[0];
+#pragma unroll
+        for (int r = 1; r < KS; ++r) {
+          const float* slot = xf + (((r - 1) * RW + w) * QB + j) * NV * kWave + lane;
+          l_i[j] = fmaf(sc[r], slot[kWave], l_i[j]);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) o[j][db][q] = a0 * o[j][db][q] + a1 * slot[(2 + 16 * db + q) * kWave];
-          m_i[j] = m;
+            for (int q = 0; q < 16; ++q) o[j][db][q] = fmaf(sc[r], slot[(2 + 16 * db + q) * kWave], o[j][db][q]);
         }
+        m_i[j] = m;
       }
     }
   }
