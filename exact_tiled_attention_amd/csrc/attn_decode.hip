@@ -9,8 +9,9 @@
 //
 // Pass 1 (split): one workgroup per (chunk, batch item, K/V head, head pass); the
 // chunk is read from HBM exactly once for the G <= 16 query heads of the pass.  Each
-// wave takes 64 keys of the chunk per pass and runs both products on the 16x16x32
-// matrix core, with the G query heads as the N dimension (only G of its 16 columns
+// wave takes 64 keys of the chunk per pass (32 for short chunks, see kShortChunk) and
+// runs both products on the 16x16x32 matrix core, with the G query heads as the N
+// dimension (only G of its 16 columns
 // carry data; the matrix core has the headroom, and the products stay off the vector
 // ALUs, which keeps the kernel bound by HBM):
 //   * every HBM load is a wave-wide 1 KiB of whole K or V rows with the streaming
@@ -41,7 +42,12 @@ static __device__ __align__(256) uint8_t scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYT
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSub = 64;   // keys per wave per pass
+// Keys per wave per pass: 64, or 32 for chunks of up to 512 keys (half the staging
+// registers and LDS, three waves per SIMD instead of two, so that more short chunks'
+// first loads are in flight at once: 0.799 -> 0.791 ms at 256-key chunks on the
+// [64 x 32 heads, 8 K/V heads, d 128] decode; at 1536-key chunks 64 keys are faster,
+// 0.677 against 0.695 ms).
+constexpr int kShortChunk = 512;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -72,14 +78,15 @@ template <int D> __device__ inline int swz_v(int r) { return D == 128 ? 2 * (r &
 // PG: K/V come from a paged pool [num_pages, Hkv, P, D] through the block table
 // (logical page i of sequence b is physical page block_table[b, i]); otherwise from
 // contiguous caches [B, Hkv, Smax, D].
-template <typename T, int D, int G, bool PG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(DecodeArgs a) {
+template <typename T, int D, int G, bool PG, int kSub>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSub == 32 ? 3 : 2))) void decode_split_kernel(DecodeArgs a) {
   constexpr int DC = D / 32;          // contraction chunks of the score product
   constexpr int DB = D / 16;          // 16-wide d blocks of the output
   constexpr int KT = kSub / 16;       // 16-key score tiles per pass
   constexpr int CPR = D / 8;          // 16-byte chunks per V row
   constexpr int VLD = kSub * CPR / 64;   // V chunks staged per lane per pass
   static_assert(G >= 1 && G <= 16, "heads per pass");
+  static_assert(kSub == 32 || kSub == 64, "keys per pass");
   typedef Mfma16<T> MF;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_v[4][kSub * D * 2];
@@ -145,8 +152,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // All of the pass's loads first, each wave-wide load 1 KiB of whole rows with the
     // streaming hint (every byte is read once); K then V go through the wave's LDS
     // region, K first.
-    // Paged: the pass's 64 keys lie in one page (P is a power of two >= 64 and base a
-    // multiple of 64); its rows of this head are contiguous.  The resource covers the
+    // Paged: the pass's kSub keys lie in one page (P is a power of two >= 64 and base a
+    // multiple of kSub); its rows of this head are contiguous.  The resource covers the
     // page rows below the sequence length, so rows past it read as zero as above.
     int row0 = base;
     if constexpr (PG) {
@@ -358,10 +365,18 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D, int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.nchunk, (unsigned)(a.B * a.Hkv), (unsigned)(a.group / G));
-  if (a.block_table != nullptr)
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G, true>), grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, G, false>), grid, dim3(kThreads), 0, stream, a);
+  const bool paged = a.block_table != nullptr;
+  if (a.chunk <= kShortChunk) {
+    if (paged)
+      hipLaunchKernelGGL((decode_split_kernel<T, D, G, true, 32>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<T, D, G, false, 32>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (paged)
+      hipLaunchKernelGGL((decode_split_kernel<T, D, G, true, 64>), grid, dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<T, D, G, false, 64>), grid, dim3(kThreads), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2((unsigned)((a.B * a.Hq + 3) / 4));
