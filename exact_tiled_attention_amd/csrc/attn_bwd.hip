@@ -170,17 +170,18 @@ constexpr int kKVT = kKW * kKG;       // keys per workgroup
 constexpr int kKVW = 2 * kKG;         // waves per workgroup
 constexpr int kKVQ = 32;              // queries per step
 
-// QS staged Q / dO slots and PSL P-handoff slots (3 and 2 in the lagged schedule).
-template <int D, int QS, int PSL>
+// QS staged Q / dO slots and PSL P-handoff slots (4 and 2 in the lagged schedule); the
+// K tile and the dS slots exist only with dQ.
+template <int D, int QS, int PSL, bool DQ>
 struct KvLds {
   static constexpr int ROWB = D * 2;
   static constexpr int QT = kKVQ * ROWB;            // one staged Q or dO tile
   static constexpr int Q0 = 0;                      // Q slots
   static constexpr int DO0 = QS * QT;               // dO slots
   static constexpr int K = 2 * QS * QT;             // K tile [128 keys][D]
-  static constexpr int DS = K + kKVT * ROWB;        // dS slots 0, 1: [128 keys][32 queries], 64-byte rows
+  static constexpr int DS = K + (DQ ? kKVT * ROWB : 0);   // dS slots 0, 1: [128 keys][32 queries], 64-byte rows
   static constexpr int DSS = 2 * kKVT * kKVQ * 2;   // one slot: the values, then their bf16 residuals
-  static constexpr int P = DS + 2 * DSS;            // P handoff [slot][group][16 registers][64 lanes] float32
+  static constexpr int P = DS + (DQ ? 2 * DSS : 0); // P handoff [slot][group][16 registers][64 lanes] float32
   static constexpr int PS = kKG * 16 * kWave * 4;   // one P slot
   static constexpr int Z = P + PSL * PS;            // dropout keep bits [role][group][64 lanes] uint32
   static constexpr int BYTES = Z + 2 * kKG * kWave * 4;
@@ -218,11 +219,15 @@ void bwd_kv_kernel(BwdArgs a) {
   typedef typename E::v8 V8;
   typedef M16<T> MF;
   // Lagged schedule (no dQ, 16-bit operands, no dropout): in step k the P waves take
-  // query tile k (S, P, dV) while the dS waves take tile k - 1 (dP, dS, dK) with the P
-  // their partners handed over a step earlier, so the two roles no longer wait for each
-  // other within a step: one barrier per step, three Q / dO slots, two P slots.
+  // query tile k (S, P, dV) while the dS waves take tile k - 1 (dP, dS) with the P their
+  // partners handed over a step earlier, and the dK product of tile k - 2 (its dS kept
+  // in registers): the roles never wait for each other within a step (one barrier per
+  // step, four Q / dO slots, two P slots), and while the P wave of a SIMD issues its S
+  // products, its exponentials and its dV products, its dS partner issues dK products,
+  // dP products and the vector work of dS, so that the matrix core and the vector ALU
+  // get work from the two waves in turn.
   constexpr bool LAG = !DQ && !F8 && !DROP;
-  typedef KvLds<D, LAG ? 3 : 2, LAG ? 2 : 1> L;
+  typedef KvLds<D, LAG ? 4 : 2, LAG ? 2 : 1, DQ> L;
   constexpr int KC = D / 16;                 // contraction chunks of S and dP
   constexpr int DB = D / 32;                 // 32-wide d blocks of dK, dV
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -231,8 +236,8 @@ void bwd_kv_kernel(BwdArgs a) {
   static_assert(WL * kWave == kKVQ * CPR && kWave % CPR == 0, "staging splits evenly");
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[LAG ? 3 : 2][kKVQ];
-  __shared__ __attribute__((aligned(16))) float s_del[LAG ? 3 : 2][kKVQ];
+  __shared__ __attribute__((aligned(16))) float s_lse[LAG ? 4 : 2][kKVQ];
+  __shared__ __attribute__((aligned(16))) float s_del[LAG ? 4 : 2][kKVQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -501,6 +506,40 @@ void bwd_kv_kernel(BwdArgs a) {
     }
   };
 
+  // Lagged dS role: dS = P (dP - D) of the step in slot sb, packed (chunk c: queries 16c +
+  // 4g + s%4 and + 8), and, a step later, its dK product against that step's Q tile.
+  auto ds_make = [&](int sb, f32x16& x, int ps, u32x4 (&hi)[2], u32x4 (&lo)[2]) {
+    const float* const phand = phand0 + ps * (L::PS / 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 dl = *reinterpret_cast<const f32x4*>(&s_del[sb][8 * j + 4 * g]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        x[i] = phand[i * kWave] * (x[i] - dl[e]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      split_pack4x2<T>(f32x4{x[8 * c + 0], x[8 * c + 1], x[8 * c + 2], x[8 * c + 3]},
+                       f32x4{x[8 * c + 4], x[8 * c + 5], x[8 * c + 6], x[8 * c + 7]}, hi[c], lo[c]);
+  };
+  auto dk_apply = [&](const u32x4 (&hi)[2], const u32x4 (&lo)[2], int sb) {
+    const uint8_t* src = lds + L::Q0 + sb * L::QT;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int r0 = 16 * c + 4 * g;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int c0 = 32 * db + 16 * gh;
+        const u32x2 t0 = tr_rows(src, r0, c0), t1 = tr_rows(src, r0 + 8, c0);
+        const V8 bt = as_v8<V8>(u32x4{t0.x, t0.y, t1.x, t1.y});
+        acc[db] = E::mfma(as_v8<V8>(hi[c]), bt, acc[db]);
+        if constexpr (kSplit<T>) acc[db] = E::mfma(as_v8<V8>(lo[c]), bt, acc[db]);
+      }
+    }
+  };
+
   // Phase 3: dQ = dS K over the tile's 128 keys in 16x16 tiles (16 queries x 16 d): wave w
   // takes query block w / 4 and TPW adjacent d blocks, so its dS reads serve all of them.
   // A = dS (lane = query column, slots = keys 32kc + 8G + s%4 and + 4, by transpose reads
@@ -555,7 +594,7 @@ void bwd_kv_kernel(BwdArgs a) {
   if constexpr (LAG) {
     // Step k: the rows of tile k are stored and tile k has landed; after the barrier
     // every wave has finished step k - 1 (P(k - 1) is visible, and the Q / dO slot of
-    // tile k - 2 is free for tile k + 1).
+    // tile k - 3 is free for tile k + 1).  One step more than tiles: the last dK.
     // coordinates of steps k - 1, k and k + 1, advanced without divisions
     int qt_prev = 0, h_k = 0, qt_k = 0, h_next = 0, qt_next = 0;
     if (nsteps > 0) step_coords(0, h_k, qt_k);
@@ -568,12 +607,13 @@ void bwd_kv_kernel(BwdArgs a) {
     h_next = h_k;
     qt_next = qt_k;
     advance(h_next, qt_next);
-    for (int k = 0; k <= nsteps; ++k) {
-      if (k < nsteps) store_rows(k % 3);
+    u32x4 dsh[2] = {}, dsl[2] = {};          // dS waves: the packed dS of the previous step
+    for (int k = 0; k <= nsteps + 1; ++k) {
+      if (k < nsteps) store_rows(k % 4);
       wait_vmcnt<0>();
       __syncthreads();
       if (k + 1 < nsteps) {
-        stage_at(h_next, qt_next, (k + 1) % 3);
+        stage_at(h_next, qt_next, (k + 1) % 4);
         fetch_rows_at(h_next, qt_next);
       }
       if (role_p) {
@@ -582,15 +622,18 @@ void bwd_kv_kernel(BwdArgs a) {
           const bool masked = key_tail || qt < cp.nomask_qtile || (qt + 1) * kKVQ > a.Sq;
           f32x16 x;
           if (masked)
-            phase1(std::true_type{}, qt, k % 3, sl2b, x, k & 1);
+            phase1(std::true_type{}, qt, k % 4, sl2b, x, k & 1);
           else
-            phase1(std::false_type{}, qt, k % 3, sl2b, x, k & 1);
-          phase2(k % 3, 1.f, x, k & 1);
+            phase1(std::false_type{}, qt, k % 4, sl2b, x, k & 1);
+          phase2(k % 4, 1.f, x, k & 1);
         }
-      } else if (k >= 1) {
-        f32x16 x;
-        phase1(std::false_type{}, qt_prev, (k - 1) % 3, sl2b, x, (k - 1) & 1);   // dP (P carries the mask)
-        phase2((k - 1) % 3, 1.f, x, (k - 1) & 1);
+      } else {
+        if (k >= 2) dk_apply(dsh, dsl, (k - 2) % 4);
+        if (k >= 1 && k <= nsteps) {
+          f32x16 x;
+          phase1(std::false_type{}, qt_prev, (k - 1) % 4, sl2b, x, (k - 1) & 1);   // dP (P carries the mask)
+          ds_make((k - 1) % 4, x, (k - 1) & 1, dsh, dsl);
+        }
       }
       qt_prev = qt_k;
       h_k = h_next;
