@@ -183,8 +183,8 @@ struct KvLds {
   static constexpr int DSS = 2 * kKVT * kKVQ * 2;   // one slot: the values, then their bf16 residuals
   static constexpr int P = DS + (DQ ? 2 * DSS : 0); // P handoff [slot][group][16 registers][64 lanes] float32
   static constexpr int PS = kKG * 16 * kWave * 4;   // one P slot
-  static constexpr int Z = P + PSL * PS;            // dropout keep bits [role][group][64 lanes] uint32
-  static constexpr int BYTES = Z + 2 * kKG * kWave * 4;
+  static constexpr int Z = P + PSL * PS;            // dropout keep bits [role][group][64 lanes] uint32 ([slot][half][group][lanes] when lagged)
+  static constexpr int BYTES = Z + 4 * kKG * kWave * 4;
 };
 
 // Chunk swizzle of staged rows (Q, dO, K): chunk p of row r at position p ^ kv_swz(r).
@@ -210,15 +210,16 @@ __device__ inline int kv_ds_off(int key, int q) {
 // the start of a step and widened into its LDS slot at the end (dO still goes straight
 // to LDS).
 // DROP: regenerate the forward's dropout decisions Z (keep / (1 - p)) and use
-// dV += (P Z)^T dO, dS = P (Z dP - D).  The dS waves draw the step's decisions while the
-// P waves compute probabilities and hand them over through LDS with P's barrier.
+// dV += (P Z)^T dO, dS = P (Z dP - D).  The roles split the Philox work: in the lagged
+// schedule the P wave draws query groups 2, 3 of its tile k and the dS wave groups 0, 1
+// of tile k + 1 a step ahead, each handing its half to the other through LDS.
 template <typename T, typename G, int D, bool CAUSAL, bool DQ, bool F8 = false, bool DROP = false>
 __global__ __launch_bounds__(kKVW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_kv_kernel(BwdArgs a) {
   typedef Elem<T> E;
   typedef typename E::v8 V8;
   typedef M16<T> MF;
-  // Lagged schedule (no dQ, 16-bit operands, no dropout): in step k the P waves take
+  // Lagged schedule (no dQ, 16-bit operands): in step k the P waves take
   // query tile k (S, P, dV) while the dS waves take tile k - 1 (dP, dS) with the P their
   // partners handed over a step earlier, and the dK product of tile k - 2 (its dS kept
   // in registers): the roles never wait for each other within a step (one barrier per
@@ -226,7 +227,7 @@ void bwd_kv_kernel(BwdArgs a) {
   // products, its exponentials and its dV products, its dS partner issues dK products,
   // dP products and the vector work of dS, so that the matrix core and the vector ALU
   // get work from the two waves in turn.
-  constexpr bool LAG = !DQ && !F8 && !DROP;
+  constexpr bool LAG = !DQ && !F8;
   typedef KvLds<D, LAG ? 4 : 2, LAG ? 2 : 1, DQ> L;
   constexpr int KC = D / 16;                 // contraction chunks of S and dP
   constexpr int DB = D / 32;                 // 32-wide d blocks of dK, dV
@@ -380,6 +381,30 @@ void bwd_kv_kernel(BwdArgs a) {
   uint32_t keep = 0;                         // dropout: this step's decisions (bit i = register i)
   int h_cur = 0;                             // this step's query head (the dropout counter)
 
+  // Dropout decisions of a step (query head h, query tile qt) for this lane's key, as bit
+  // i for query 8(i/4) + 4g + i%4; draw_at(h, qt, j0) makes query groups j0 and j0 + 1.
+  // The four lanes of a key quad (n = 4c .. 4c+3) share the Philox counter word key / 4:
+  // lane e = n % 4 makes the call of query 8j + 4g + e, and in round r it sends word
+  // (e + r) % 4 and receives, from quad lane (e - r) % 4, word e (its own key) of that
+  // lane's query.
+  auto draw_at = [&](int h, int qt, int j0) -> uint32_t {
+    const int e = n & 3;
+    uint32_t kb = 0;
+#pragma unroll
+    for (int j = j0; j < j0 + 2; ++j) {
+      const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qt * kKVQ + 8 * j + 4 * g + e),
+                                     (uint32_t)(b * a.Hq + h), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int wi = (e + r) & 3;
+        const uint32_t send = wi == 0 ? wv[0] : wi == 1 ? wv[1] : wi == 2 ? wv[2] : wv[3];
+        const uint32_t got = (uint32_t)__shfl((int)send, (lane & ~3) | ((e - r) & 3));
+        kb |= (got >= a.drop.thresh ? 1u : 0u) << (4 * j + ((e - r) & 3));
+      }
+    }
+    return kb;
+  };
+
   // Phase 1: S (role P) or dP (role dS) for the group's 32 keys: A = Q / dO rows (row n,
   // chunk 2kc + g) of the staged tile, B = the group's K / V fragments.  Role P turns S
   // into P (masked) and hands it to its partner.
@@ -393,31 +418,11 @@ void bwd_kv_kernel(BwdArgs a) {
       const V8 af = as_v8<V8>(ld_lds_16(src + n * L::ROWB + (((2 * kc + g) ^ kv_swz<D>(n)) * 16)));
       x = E::mfma(af, bf[kc], x);
     }
-    // Dropout decisions of the step for this lane's key, as bit i for query 8(i/4) + 4g +
-    // i%4; draw(j0) makes query groups j0 and j0 + 1.  The four lanes of a key quad
-    // (n = 4c .. 4c+3) share the Philox counter word key / 4: lane e = n % 4 makes the call
-    // of query 8j + 4g + e, and in round r it sends word (e + r) % 4 and receives, from
-    // quad lane (e - r) % 4, word e (its own key) of that lane's query.  The roles split
-    // the draws: the dS wave makes groups 0, 1 after its dP product, the P wave groups 2, 3
-    // after its probabilities; each hands its half to the partner through LDS.
-    auto draw = [&](int j0) -> uint32_t {
-      const int e = n & 3;
-      uint32_t kb = 0;
-#pragma unroll
-      for (int j = j0; j < j0 + 2; ++j) {
-        const u32x4 wv = philox4x32_10((uint32_t)mykey >> 2, (uint32_t)(qt * kKVQ + 8 * j + 4 * g + e),
-                                       (uint32_t)(b * a.Hq + h_cur), a.drop.offset, a.drop.seed_lo, a.drop.seed_hi);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int wi = (e + r) & 3;
-          const uint32_t send = wi == 0 ? wv[0] : wi == 1 ? wv[1] : wi == 2 ? wv[2] : wv[3];
-          const uint32_t got = (uint32_t)__shfl((int)send, (lane & ~3) | ((e - r) & 3));
-          kb |= (got >= a.drop.thresh ? 1u : 0u) << (4 * j + ((e - r) & 3));
-        }
-      }
-      return kb;
-    };
-    if (DROP && !role_p) {
+    // Two-barrier schedule: the roles split the step's dropout draws, the dS wave making
+    // query groups 0, 1 after its dP product, the P wave groups 2, 3 after its
+    // probabilities; each hands its half to the partner through LDS.
+    auto draw = [&](int j0) -> uint32_t { return draw_at(h_cur, qt, j0); };
+    if (DROP && !LAG && !role_p) {
       keep = draw(0);
       zhand[0] = keep;
     }
@@ -439,7 +444,7 @@ void bwd_kv_kernel(BwdArgs a) {
           phand[i * kWave] = pv;
         }
       }
-      if constexpr (DROP) {
+      if constexpr (DROP && !LAG) {
         keep = draw(2);
         zhand[kKG * kWave] = keep;
       }
@@ -455,7 +460,7 @@ void bwd_kv_kernel(BwdArgs a) {
     uint8_t* dsv = lds + L::DS + sb * L::DSS;
     uint8_t* dsr = dsv + L::DSS / 2;
     const uint8_t* src = lds + (role_p ? L::DO0 : L::Q0) + sb * L::QT;
-    if constexpr (DROP) {
+    if constexpr (DROP && !LAG) {
       keep |= role_p ? zhand[0] : zhand[kKG * kWave];
     }
     if (!role_p) {
@@ -516,7 +521,8 @@ void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * j + e;
-        x[i] = phand[i * kWave] * (x[i] - dl[e]);
+        const float z = DROP ? (((keep >> i) & 1u) ? a.drop.rp : 0.f) : 1.f;
+        x[i] = phand[i * kWave] * (z * x[i] - dl[e]);
       }
     }
 #pragma unroll
@@ -608,6 +614,13 @@ void bwd_kv_kernel(BwdArgs a) {
     qt_next = qt_k;
     advance(h_next, qt_next);
     u32x4 dsh[2] = {}, dsl[2] = {};          // dS waves: the packed dS of the previous step
+    // dropout halves [slot][half][group][lane]: half 0 (groups 2, 3) from the P wave of the
+    // tile, half 1 (groups 0, 1) from the dS wave a step ahead; slot = tile & 1
+    uint32_t* const zs = reinterpret_cast<uint32_t*>(lds + L::Z) + grp * kWave + lane;
+    auto zslot = [&](int slot, int half) { return zs + (2 * slot + half) * (kKG * kWave); };
+    if constexpr (DROP) {
+      if (!role_p && nsteps > 0) *zslot(0, 1) = draw_at(h_k, qt_k, 0);
+    }
     for (int k = 0; k <= nsteps + 1; ++k) {
       if (k < nsteps) store_rows(k % 4);
       wait_vmcnt<0>();
@@ -625,15 +638,25 @@ void bwd_kv_kernel(BwdArgs a) {
             phase1(std::true_type{}, qt, k % 4, sl2b, x, k & 1);
           else
             phase1(std::false_type{}, qt, k % 4, sl2b, x, k & 1);
+          if constexpr (DROP) {
+            const uint32_t half0 = draw_at(h, qt, 2);
+            *zslot(k & 1, 0) = half0;
+            keep = half0 | *zslot(k & 1, 1);
+          }
           phase2(k % 4, 1.f, x, k & 1);
         }
       } else {
         if (k >= 2) dk_apply(dsh, dsl, (k - 2) % 4);
+        uint32_t half1 = 0;
+        if (DROP && k + 1 < nsteps) half1 = draw_at(h_next, qt_next, 0);
         if (k >= 1 && k <= nsteps) {
           f32x16 x;
           phase1(std::false_type{}, qt_prev, (k - 1) % 4, sl2b, x, (k - 1) & 1);   // dP (P carries the mask)
+          if constexpr (DROP) keep = *zslot((k - 1) & 1, 0) | *zslot((k - 1) & 1, 1);
           ds_make((k - 1) % 4, x, (k - 1) & 1, dsh, dsl);
         }
+        // tile k + 1's half goes where tile k - 1's was, after that was read above
+        if (DROP && k + 1 < nsteps) *zslot((k + 1) & 1, 1) = half1;
       }
       qt_prev = qt_k;
       h_k = h_next;
