@@ -125,7 +125,7 @@ void fwd_kernel(FwdArgs a) {
   static_assert(TL::CHUNKS % NTK == 0 && LOADS >= 1, "chunks must split evenly over the threads");
   static_assert(KC % PC == 0, "score product must split evenly over the key chunks");
   constexpr int NV = 2 + 16 * DB;             // merged values per lane and query block
-  constexpr int MERGE = (KS - 1) * RW * QB * NV * kWave * 4;   // states of key ranges 1 .. KS-1
+  constexpr int MERGE = (D == 64 ? KS : KS - 1) * RW * QB * NV * kWave * 4;   // the key ranges' states
   constexpr int LDS = (KS > 1 && MERGE > KS * RING) ? MERGE : KS * RING;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_all[LDS];
@@ -550,10 +550,81 @@ void fwd_kernel(FwdArgs a) {
   }
 
   wait_vmcnt<0>();   // no ring load may still be in flight when the LDS is reused
-  if constexpr (KS > 1) {
+  if constexpr (KS > 1 && D == 64) {
+    // Merge the key ranges' states of each row in one max frame ("M4.3 - IO-Aware
+    // Attention ...", section 0x08B), then O = u / l and LSE = (m + log2 l) ln 2 (FA2
+    // section 0x02D).  Every range hands its (m, l, u) over through LDS, and every range
+    // then finishes its share of the output: units of four columns (one 8-byte store per
+    // lane), unit u = 4 db + r4 going to range u % KS, so no range waits for another to
+    // finish all the columns.  Layout [range][wave][block][value][lane] keeps lanes on
+    // banks.
+    float* xf = reinterpret_cast<float*>(lds_all);
+    __syncthreads();                                   // the rings are free
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      float* slot = xf + ((kh * RW + w) * QB + j) * NV * kWave + lane;
+      slot[0] = m_i[j];
+      slot[kWave] = l_i[j];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) slot[(2 + 16 * db + q) * kWave] = o[j][db][q];
+    }
+    __syncthreads();
+    constexpr int RSTR = RW * QB * NV * kWave;        // floats between two ranges' states
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const float* st = xf + (w * QB + j) * NV * kWave + lane;   // range r at st + r RSTR
+      float mr[KS], sc[KS];
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < KS; ++r) {
+        mr[r] = st[r * RSTR];
+        m = fmaxf(m, mr[r]);
+      }
+      float l = 0.f;
+#pragma unroll
+      for (int r = 0; r < KS; ++r) {
+        sc[r] = (m == -INFINITY) ? 0.f : fast_exp2(mr[r] - m);
+        l = fmaf(sc[r], st[r * RSTR + kWave], l);
+      }
+      const float l_tot = l + __shfl_xor(l, 32);
+      const bool empty = (m == -INFINITY) || !(l_tot > 0.f);
+      const float inv = empty ? 0.f : (DROP ? a.drop.rp : 1.f) / l_tot;
+      if (qrow[j] < Sq) {
+        T* ob = reinterpret_cast<T*>(a.o) + q_off + (int64_t)qrow[j] * q_rs;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            if ((4 * db + r4) % KS != kh) continue;
+            float v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              float acc = 0.f;
+#pragma unroll
+              for (int r = 0; r < KS; ++r) acc = fmaf(sc[r], st[r * RSTR + (2 + 16 * db + 4 * r4 + k) * kWave], acc);
+              v[k] = acc * inv;
+            }
+            u32x2 pk;
+            pk.x = E::pack2(v[0], v[1]);
+            pk.y = E::pack2(v[2], v[3]);
+            *reinterpret_cast<u32x2*>(ob + db * 32 + 8 * r4 + 4 * grp) = pk;
+          }
+        }
+        if (kh == 0 && a.lse != nullptr && grp == 0) {
+          a.lse[lse_off + qrow[j]] = empty ? -INFINITY : (m + __log2f(l_tot)) * ATTN_LN2;
+        }
+      }
+    }
+    return;
+  }
+
+  if constexpr (KS > 1 && D != 64) {
     // Merge the key ranges' states of each row in one max frame ("M4.3 - IO-Aware
     // Attention ...", section 0x08B): ranges 1 .. KS-1 hand their (m, l, u) to range 0
-    // through LDS, all at once, and range 0 combines them.  Layout
+    // through LDS, all at once, and range 0 combines them (at d = 128 the shared
+    // epilogue above costs the dropout form a spilled register).  Layout
     // [range][wave][block][value][lane] keeps lanes on banks.
     float* xf = reinterpret_cast<float*>(lds_all);
     __syncthreads();                                   // the rings are free
